@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 block-scaled batched GEMV on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+
+A step is one GEMV call (the whole path: A/SFA stream, b' staging, decode,
+FMA, reduction, float16 store) over one input set. Input sets are seeded,
+synthetic and already resident in HBM; consecutive steps rotate through enough
+distinct sets (>= 512 MiB together) that neither the L2s nor the 256 MiB
+Infinity Cache hold the next step's operands.
+
+Timing:
+  * timed region: exactly K steps captured in one HIP graph (so host launch
+    overhead is not measured), replayed once between two synchronisations;
+    GPU time from events around the replay gives ms_per_step and ``value``.
+  * per-kernel duration for the roofline: the same K calls launched eagerly,
+    each between two events on the launch stream, behind a spin kernel that
+    lets the host queue them all first.
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak) for NVFP4 GEMV 7168×16384×1"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+ROTATE_BYTES = 512 * 2 ** 20
+WORKLOADS = {"headline": synth.HEADLINE, "balanced": synth.BALANCED, "batched": synth.BATCHED,
+             "tiny": synth.TINY}
+for _w in synth.EDGE:
+    WORKLOADS[_w.name] = _w
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    src = os.path.join(ROOT, "block_scaled_fp4_gemv_amd", "csrc", "nvfp4_gemv.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload_name: str, layout: str):
+    """HBM traffic per launch from a committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}_{layout}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, layout: str, budget_s: float):
+    """The oracle as it stands, on this host's cores, on input set 0."""
+    import oracle
+    oracle.build(force=False)
+    cores = min(os.cpu_count() or 1, 16)
+    inp = synth.make_inputs(w, 0)
+    # bounded sample: whole calls if one fits the budget, else a row subset
+    t0 = time.perf_counter()
+    oracle.gemv_rows(inp, np.arange(min(256, w.M * w.L)), layout, nthreads=cores)
+    per_row = (time.perf_counter() - t0) / min(256, w.M * w.L)
+    rows_total = w.M * w.L
+    if per_row * rows_total <= budget_s / 2:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gemv(inp, layout, nthreads=cores)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 50:
+                break
+        sec_per_call = el / reps
+        sample = f"{reps} full {w.name} calls on input set 0 ({layout} scales)"
+    else:
+        nrows = max(1, int(budget_s / per_row))
+        rows = np.arange(nrows) % rows_total
+        t0 = time.perf_counter()
+        oracle.gemv_rows(inp, rows, layout, nthreads=cores)
+        el = time.perf_counter() - t0
+        sec_per_call = el / nrows * rows_total
+        sample = f"{nrows} of {rows_total} rows of {w.name} input set 0, scaled to a full call"
+    return {"value": round(w.ideal_bytes / sec_per_call / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle", "sample": sample,
+            "us_per_call": round(sec_per_call * 1e6, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
+    ap.add_argument("--layout", default="blocked", choices=["blocked", "plain"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this GEMV is built and timed on a single "
+              "MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp4_gemv_amd as g
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    layout = args.layout
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+
+    # ---- rotating input sets, resident in HBM
+    per_set = w.ideal_read_bytes
+    nsets = max(1, min(64, -(-ROTATE_BYTES // per_set)))
+    log(f"workload {w.name}: {nsets} input sets of {per_set / 1e6:.1f} MB")
+    sets = []
+    for i in range(nsets):
+        inp = synth.make_inputs(w, i)
+        sets.append(dict(
+            a=torch.from_numpy(inp.a).to(dev), b=torch.from_numpy(inp.b).to(dev),
+            sfa=torch.from_numpy(inp.sfa(layout)).to(dev), sfb=torch.from_numpy(inp.sfb(layout)).to(dev),
+            c=torch.empty(w.L * w.M, dtype=torch.float16, device=dev)))
+        if i == 0:
+            inp0 = inp
+    torch.cuda.synchronize()
+    M, K, L = w.M, w.K, w.L
+    plan = g.nvfp4_gemv_plan(M, K, L)
+    log(f"plan: {plan}")
+
+    def step(i, stream=None):
+        s = sets[i % nsets]
+        g.nvfp4_gemv(s["a"], s["b"], s["sfa"], s["sfb"], s["c"], M, K, L, layout, stream)
+
+    # ---- warmup (also allocates any split-K workspace before graph capture)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- correctness of the benchmarked configuration (set 0) against the oracle
+    verified = None
+    if not args.no_verify:
+        import oracle
+        oracle.build(force=False)
+        step(0)
+        torch.cuda.synchronize()
+        got = sets[0]["c"].cpu().view(torch.int16).numpy().view(np.uint16).reshape(L, M)
+        ref = oracle.gemv(inp0, layout, nthreads=min(os.cpu_count() or 1, 16))
+        verified = bool(oracle.check(got, ref).all())
+        log(f"parity vs oracle on set 0: {'ok' if verified else 'FAILED'}")
+
+    # ---- timed region: exactly K steps in one graph
+    K_steps = args.steps
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(K_steps):
+            step(i)
+    torch.cuda.synchronize()
+    graph.replay()                       # untimed replay: graph upload
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / K_steps
+    log(f"timed: {K_steps} steps, {gpu_ms:.3f} ms GPU ({wall_s * 1e3:.3f} ms wall)")
+
+    # ---- per-kernel durations: eager launches bracketed by events
+    st = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2e8))       # let the host queue every launch first
+    for i in range(K_steps):
+        starts[i].record(st)
+        step(i, st)
+        ends[i].record(st)
+    torch.cuda.synchronize()
+    durs_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
+    kern_avg, kern_med = float(durs_us.mean()), float(np.median(durs_us))
+    log(f"kernel: avg {kern_avg:.2f} us, median {kern_med:.2f} us, min {durs_us.min():.2f}, "
+        f"p90 {np.percentile(durs_us, 90):.2f}")
+
+    ideal = w.ideal_bytes
+    value_gbs = ideal / (ms_per_step * 1e-3) / 1e9
+    achieved = ideal / (kern_avg * 1e-6) / 1e9
+    traffic = traffic_from_profile(w.name, layout)
+    out = {
+        "metric": METRIC,
+        "value": round(value_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "K": K, "L": L, "N": 1, "sf_layout": layout,
+                   "rotating_sets": nsets, "ideal_bytes_per_call": ideal, "plan": plan},
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "pct_of_peak": round(100 * value_gbs / PEAK_HBM_GBS, 2),
+        "kernel_us": {"avg": round(kern_avg, 3), "median": round(kern_med, 3),
+                      "min": round(float(durs_us.min()), 3),
+                      "p90": round(float(np.percentile(durs_us, 90)), 3)},
+        "verified_vs_oracle": verified,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+        "context": {"b200_target_us_from_pages": {"headline_7168x16384x1": 8.6,
+                                                  "batched_4096x7168x8": 17.3,
+                                                  "balanced_7168x2048x4": 4.3}},
+        "device": props.name,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(w, layout, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+"""Python binding of the MI355X NVFP4 block-scaled batched GEMV (libnvfp4gemv.so).
+
+Argument marshalling only: every step of the GEMV runs in the HIP library. The
+names mirror the C ABI in include/nvfp4_gemv.h. torch provides device memory and
+the stream; tensors are passed as raw device pointers.
+
+    nvfp4_gemv(a, b, sfa, sfb, c, M, K, L, sf_layout, stream=None)
+
+    a   uint8 [L, M, K/2]   packed E2M1, low nibble = even k
+    b   uint8 [L, K/2]
+    sfa uint8 plain [L, M, K/16] or blocked [L, ceil(M/128)*ceil(K/64)*512]
+    sfb uint8 plain [L, K/16]    or blocked [L, ceil(K/64)*512]
+    c   float16 [L, M]          written
+
+There is no fallback: if the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libnvfp4gemv.so")
+
+NVFP4_SF_PLAIN = 0
+NVFP4_SF_BLOCKED = 1
+NVFP4_OK = 0
+NVFP4_ERR_NULL_POINTER = 1
+NVFP4_ERR_INVALID_SHAPE = 2
+NVFP4_ERR_MISALIGNED = 3
+NVFP4_ERR_INVALID_LAYOUT = 4
+NVFP4_ERR_WORKSPACE = 5
+NVFP4_ERR_HIP = 6
+
+EXPORTED_SYMBOLS = (
+    "nvfp4_gemv",
+    "nvfp4_gemv_workspace_bytes",
+    "nvfp4_gemv_ex",
+    "nvfp4_gemv_plan",
+    "nvfp4_status_string",
+    "nvfp4_last_hip_error",
+)
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = status_string(status)
+        if status == NVFP4_ERR_HIP:
+            msg += f" (hipError_t {lib().nvfp4_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [status {status}]")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("lanes_per_row", ctypes.c_int32),
+                ("rows_per_wg", ctypes.c_int32),
+                ("k_splits", ctypes.c_int32),
+                ("k_per_split", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64),
+                ("threads_per_wg", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_scaled_fp4_gemv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.nvfp4_gemv.restype = i32
+    L.nvfp4_gemv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.nvfp4_gemv_ex.restype = i32
+    L.nvfp4_gemv_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
+    L.nvfp4_gemv_workspace_bytes.restype = ctypes.c_size_t
+    L.nvfp4_gemv_workspace_bytes.argtypes = [i64, i64, i64]
+    L.nvfp4_gemv_plan.restype = i32
+    L.nvfp4_gemv_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_status_string.argtypes = [i32]
+    L.nvfp4_last_hip_error.restype = i32
+    L.nvfp4_last_hip_error.argtypes = []
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().nvfp4_status_string(status).decode()
+
+
+def layout_id(layout) -> int:
+    if layout in (NVFP4_SF_PLAIN, "plain"):
+        return NVFP4_SF_PLAIN
+    if layout in (NVFP4_SF_BLOCKED, "blocked"):
+        return NVFP4_SF_BLOCKED
+    return int(layout)   # passed through; the library rejects unknown values
+
+
+def cdiv(a: int, b: int) -> int:
+    return (a + b - 1) // b
+
+
+def operand_bytes(M: int, K: int, L: int, layout) -> dict:
+    """Bytes each operand must hold for a shape."""
+    lay = layout_id(layout)
+    nkb = K // 16
+    if lay == NVFP4_SF_BLOCKED:
+        sfa = L * cdiv(M, 128) * cdiv(nkb, 4) * 512
+        sfb = L * cdiv(nkb, 4) * 512
+    else:
+        sfa, sfb = L * M * nkb, L * nkb
+    return {"a": L * M * K // 2, "b": L * K // 2, "sfa": sfa, "sfb": sfb, "c": 2 * L * M}
+
+
+def _ptr_and_bytes(x):
+    """(device pointer, byte size) of a torch tensor, or (x, None) for a raw int."""
+    if x is None:
+        return None, None
+    if isinstance(x, int):
+        return x, None
+    if not x.is_cuda:
+        raise ValueError("operands must be device tensors")
+    if not x.is_contiguous():
+        raise ValueError("operands must be contiguous")
+    return x.data_ptr(), x.numel() * x.element_size()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check_sizes(M, K, L, layout, **ops):
+    if M < 1 or K < 1 or L < 1 or K % 32:
+        return   # the library reports shape errors itself
+    need = operand_bytes(M, K, L, layout)
+    for name, nbytes in ops.items():
+        if nbytes is not None and nbytes < need[name]:
+            raise ValueError(f"{name} holds {nbytes} bytes, the shape needs {need[name]}")
+
+
+def nvfp4_gemv(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, stream=None) -> None:
+    """Enqueue c = GEMV(a, b, sfa, sfb) on ``stream`` (default: torch's current stream)."""
+    (pa, na), (pb, nb), (psa, nsa), (psb, nsb), (pc, nc) = map(_ptr_and_bytes, (a, b, sfa, sfb, c))
+    lay = layout_id(sf_layout)
+    _check_sizes(M, K, L, lay, a=na, b=nb, sfa=nsa, sfb=nsb, c=nc)
+    st = lib().nvfp4_gemv(pa, pb, psa, psb, pc, M, K, L, lay, _stream_handle(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemv")
+
+
+def nvfp4_gemv_workspace_bytes(M: int, K: int, L: int) -> int:
+    return int(lib().nvfp4_gemv_workspace_bytes(M, K, L))
+
+
+def nvfp4_gemv_ex(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, workspace,
+                  workspace_bytes: int | None = None, stream=None) -> None:
+    """As nvfp4_gemv with a caller-owned (zero-initialised) workspace."""
+    (pa, na), (pb, nb), (psa, nsa), (psb, nsb), (pc, nc) = map(_ptr_and_bytes, (a, b, sfa, sfb, c))
+    pw, nw = _ptr_and_bytes(workspace)
+    if workspace_bytes is None:
+        workspace_bytes = nw or 0
+    lay = layout_id(sf_layout)
+    _check_sizes(M, K, L, lay, a=na, b=nb, sfa=nsa, sfb=nsb, c=nc)
+    st = lib().nvfp4_gemv_ex(pa, pb, psa, psb, pc, M, K, L, lay, pw, workspace_bytes,
+                             _stream_handle(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemv_ex")
+
+
+def nvfp4_gemv_plan(M: int, K: int, L: int) -> dict:
+    plan = Plan()
+    st = lib().nvfp4_gemv_plan(M, K, L, ctypes.byref(plan))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemv_plan")
+    return plan.as_dict()
+
+
+def nvfp4_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def nvfp4_last_hip_error() -> int:
+    return int(lib().nvfp4_last_hip_error())

@@ -1,0 +1,135 @@
+/*
+ * nvfp4_gemv.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled batched GEMV.
+ *
+ * Operation (kernelbot NVFP4 GEMV, submission 103289, `cute_kernel`: each k
+ * contributes a * sfa * b * sfb, the contributions of one output row are
+ * accumulated in float32 and the sum is cast to float16):
+ *
+ *   c[l][m] = fp16( sum_{k<K} e2m1(A[l][m][k]) * e4m3(SFA[l][m][k/16])
+ *                            * e2m1(B[l][k])    * e4m3(SFB[l][k/16]) )
+ *
+ * for m < M, l < L (N = 1). Element format: E2M1 (Float4E2M1FN), packed two per
+ * byte along k, the even k in the low nibble. Scale format: E4M3 (Float8E4M3FN),
+ * one scale per 16 consecutive k. Accumulation is float32; the cast to float16
+ * rounds to nearest even and overflows to +-inf. Summation order inside a row
+ * is the library's own (all products are exact; partial sums round in float32),
+ * and it does not depend on the scale layout.
+ *
+ * Memory order of every operand is batch-outermost and dense (the CuTe layouts
+ * of submission 103289 `cute_jit_kernel`: A stride (K, 1, M*K), C stride
+ * (1, 1, M)):
+ *
+ *   a    uint8  [L][M][K/2]     packed E2M1 codes of A
+ *   b    uint8  [L][K/2]        packed E2M1 codes of the vector B
+ *   c    fp16   [L][M]          output (IEEE binary16 bits), written
+ *   sfa, sfb in one of two layouts, chosen by sf_layout for both:
+ *     NVFP4_SF_PLAIN:   sfa uint8 [L][M][K/16], sfb uint8 [L][K/16]
+ *     NVFP4_SF_BLOCKED: the 128x4 blocked ("permuted") layout of submission
+ *       69953 `to_blocked_batch` (equivalently submission 69575
+ *       `blocked_transform_kernel`, and the 6-D tensor of submission 103289
+ *       `permuted_to_blocked`), per batch, batches back to back:
+ *         scale (r, kb) of a rows x (K/16) matrix is at byte
+ *           ((r/128)*ceil(K/64) + kb/4)*512 + (r%32)*16 + ((r%128)/32)*4 + kb%4
+ *         sfa: rows = M, ceil(M/128)*ceil(K/64)*512 bytes per batch
+ *         sfb: rows = 1, ceil(K/64)*512 bytes per batch (B padded to 128 rows)
+ *       Padding bytes (rows >= M, columns >= K/16) are never read.
+ *
+ * Conventions shared by all entry points:
+ *   - a, b, sfa, sfb, c and workspace are DEVICE pointers owned by the caller;
+ *     the library keeps no reference to them after the call returns.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise. Faults inside the kernel surface later on
+ *     the stream.
+ *   - Every argument is validated before any HIP call; on failure nothing is
+ *     launched and a nonzero nvfp4_status_t is returned.
+ *   - Requirements: M, K, L >= 1; K % 32 == 0; L*M*K/2 < 2^62; a and b 16-byte
+ *     aligned; sfa and sfb 4-byte aligned; c 2-byte aligned.
+ */
+#ifndef NVFP4_GEMV_H
+#define NVFP4_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_SF_PLAIN = 0,
+    NVFP4_SF_BLOCKED = 1
+} nvfp4_sf_layout_t;
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL_POINTER = 1,     /* a required pointer is NULL                 */
+    NVFP4_ERR_INVALID_SHAPE = 2,    /* M, K or L out of range, or K % 32 != 0      */
+    NVFP4_ERR_MISALIGNED = 3,       /* a pointer misses its required alignment     */
+    NVFP4_ERR_INVALID_LAYOUT = 4,   /* sf_layout is not an nvfp4_sf_layout_t       */
+    NVFP4_ERR_WORKSPACE = 5,        /* workspace missing, misaligned or too small  */
+    NVFP4_ERR_HIP = 6               /* a HIP call failed; see nvfp4_last_hip_error */
+} nvfp4_status_t;
+
+/*
+ * Batched GEMV as defined above. If the problem is split along K (small M*L),
+ * float32 partial sums go to a workspace that the library allocates on first
+ * need, per device, grows on demand (with a device synchronisation) and keeps
+ * until the process ends. Calls that overlap in time on one device therefore
+ * must not use this entry point concurrently from two streams; use
+ * nvfp4_gemv_ex with separate workspaces instead.
+ */
+nvfp4_status_t nvfp4_gemv(const void *a, const void *b, const void *sfa, const void *sfb,
+                          void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
+                          void *stream);
+
+/*
+ * Workspace bytes nvfp4_gemv_ex needs for this shape (0 when the shape is not
+ * split along K). The value depends only on M, K and L.
+ */
+size_t nvfp4_gemv_workspace_bytes(int64_t M, int64_t K, int64_t L);
+
+/*
+ * As nvfp4_gemv, with a caller-owned device workspace of at least
+ * nvfp4_gemv_workspace_bytes(M, K, L) bytes, 256-byte aligned (may be NULL
+ * when that size is 0). The workspace must be zero-filled before its first use;
+ * every completed call leaves its counter region zero again, so it can be reused
+ * for any later shape without clearing. Two calls may share a workspace only
+ * if they are ordered on one stream.
+ */
+nvfp4_status_t nvfp4_gemv_ex(const void *a, const void *b, const void *sfa, const void *sfb,
+                             void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Launch plan chosen for a shape (for tests and reports). Returns NVFP4_OK and
+ * fills the fields, or an error status for an invalid shape.
+ *   lanes_per_row  lanes that share one output row (1..64)
+ *   rows_per_wg    output rows per workgroup
+ *   k_splits       number of K-slices (1 = no split)
+ *   k_per_split    K-elements per slice
+ *   workgroups     grid size; threads_per_wg threads each
+ *   lds_bytes      dynamic LDS per workgroup
+ */
+typedef struct {
+    int32_t lanes_per_row;
+    int32_t rows_per_wg;
+    int32_t k_splits;
+    int32_t k_per_split;
+    int64_t workgroups;
+    int32_t threads_per_wg;
+    int32_t lds_bytes;
+} nvfp4_plan_t;
+
+nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan);
+
+/* Static description of a status code (never NULL). */
+const char *nvfp4_status_string(int status);
+
+/* The hipError_t of the last failed HIP call in this thread (0 if none). */
+int nvfp4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_GEMV_H */

@@ -1,0 +1,161 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, validates arguments before any HIP call, and plans shapes sanely.
+No compute call is made here (there is no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_gemv_amd as g
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_gemv.h")
+
+A16 = 0x10000       # fake but aligned device addresses: validation never dereferences them
+OK_ARGS = dict(a=A16, b=A16 + 0x100, sfa=A16 + 0x200, sfb=A16 + 0x300, c=A16 + 0x400)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_binding_lists():
+    assert header_functions() == sorted(g.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_header_symbol():
+    lib = g.lib()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {g.LIB_PATH}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def call(**kw):
+    args = dict(OK_ARGS, M=128, K=256, L=1, layout=0)
+    args.update(kw)
+    return g.lib().nvfp4_gemv(args["a"], args["b"], args["sfa"], args["sfb"], args["c"],
+                              args["M"], args["K"], args["L"], args["layout"], None)
+
+
+@pytest.mark.parametrize("ptr", ["a", "b", "sfa", "sfb", "c"])
+def test_null_pointers(ptr):
+    assert call(**{ptr: None}) == g.NVFP4_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("M,K,L", [(0, 256, 1), (128, 0, 1), (128, 256, 0), (-1, 256, 1),
+                                   (128, 48, 1), (128, 16, 1), (128, 100, 1), (2 ** 40, 256, 1),
+                                   (1, 2 ** 40, 1), (1 << 20, 1 << 20, 1 << 20)])
+def test_bad_shapes(M, K, L):
+    assert call(M=M, K=K, L=L) == g.NVFP4_ERR_INVALID_SHAPE
+
+
+@pytest.mark.parametrize("ptr,off", [("a", 8), ("b", 4), ("sfa", 2), ("sfb", 1), ("c", 1)])
+def test_misaligned(ptr, off):
+    assert call(**{ptr: OK_ARGS[ptr] + off}) == g.NVFP4_ERR_MISALIGNED
+
+
+def test_alignment_minimums_accepted_by_validation():
+    # 4-byte aligned scales and 2-byte aligned c pass validation (they then
+    # fail later only because there is no GPU here, never with MISALIGNED)
+    st = call(sfa=OK_ARGS["sfa"] + 4, sfb=OK_ARGS["sfb"] + 4, c=OK_ARGS["c"] + 2)
+    assert st not in (g.NVFP4_ERR_MISALIGNED, g.NVFP4_ERR_NULL_POINTER, g.NVFP4_ERR_INVALID_SHAPE)
+
+
+@pytest.mark.parametrize("layout", [2, -1, 99])
+def test_bad_layout(layout):
+    assert call(layout=layout) == g.NVFP4_ERR_INVALID_LAYOUT
+
+
+def test_ex_workspace_errors():
+    lib = g.lib()
+    M, K, L = 127, 16384, 1
+    need = lib.nvfp4_gemv_workspace_bytes(M, K, L)
+    assert need > 0
+    base = (OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"], OK_ARGS["c"], M, K, L, 1)
+    assert lib.nvfp4_gemv_ex(*base, None, need, None) == g.NVFP4_ERR_WORKSPACE
+    assert lib.nvfp4_gemv_ex(*base, 0x200000, need - 1, None) == g.NVFP4_ERR_WORKSPACE
+    assert lib.nvfp4_gemv_ex(*base, 0x200010, need, None) == g.NVFP4_ERR_WORKSPACE
+    # shape errors take precedence and need no workspace
+    assert lib.nvfp4_gemv_ex(*base[:5], M, 33, L, 1, None, 0, None) == g.NVFP4_ERR_INVALID_SHAPE
+
+
+def test_workspace_bytes():
+    lib = g.lib()
+    for w in (synth.BALANCED, synth.BATCHED, synth.HEADLINE, synth.TINY):
+        assert lib.nvfp4_gemv_workspace_bytes(w.M, w.K, w.L) == 0, w.name
+    assert lib.nvfp4_gemv_workspace_bytes(0, 256, 1) == 0
+    assert lib.nvfp4_gemv_workspace_bytes(127, 16384, 1) % 256 == 0
+
+
+@pytest.mark.parametrize("w", synth.ALL, ids=lambda w: w.name)
+def test_plans(w):
+    p = g.nvfp4_gemv_plan(w.M, w.K, w.L)
+    assert 1 <= p["lanes_per_row"] <= 64
+    assert p["k_splits"] >= 1
+    assert p["k_per_split"] % 32 == 0
+    assert p["k_splits"] * p["k_per_split"] >= w.K > (p["k_splits"] - 1) * p["k_per_split"]
+    tiles = synth.ceil_div(w.M, p["rows_per_wg"])
+    assert p["workgroups"] == tiles * w.L * p["k_splits"]
+    assert p["lds_bytes"] <= 32 * 1024
+    assert p["threads_per_wg"] == 256
+
+
+def test_long_k_is_segmented_not_split():
+    # K beyond the 16384-element LDS segment no longer forces a K-split
+    p = g.nvfp4_gemv_plan(7168, 65536, 1)
+    assert p["k_splits"] == 1 and p["k_per_split"] == 65536 and p["lds_bytes"] == 32768
+
+
+def test_split_only_for_small_grids():
+    for M, K, L in [(127, 16384, 1), (1000, 4096, 3), (1, 32768, 1), (5, 65536, 2)]:
+        p = g.nvfp4_gemv_plan(M, K, L)
+        tiles = synth.ceil_div(M, p["rows_per_wg"])
+        if p["k_splits"] > 1:
+            assert tiles * L < 512
+            assert g.nvfp4_gemv_workspace_bytes(M, K, L) >= 4096
+
+
+def test_headline_plan_has_no_split():
+    p = g.nvfp4_gemv_plan(7168, 16384, 1)
+    assert p["k_splits"] == 1 and p["lanes_per_row"] == 64
+
+
+def test_plan_rejects_bad_shape():
+    with pytest.raises(g.Nvfp4Error):
+        g.nvfp4_gemv_plan(128, 100, 1)
+
+
+def test_status_strings():
+    for st in range(0, 7):
+        assert g.status_string(st)
+    assert g.status_string(1234) == "unknown status"
+
+
+def test_binding_checks_buffer_sizes():
+    # size checks happen in the binding before the library is called
+    class Fake:
+        is_cuda = True
+
+        def __init__(self, n):
+            self.n = n
+
+        def is_contiguous(self):
+            return True
+
+        def data_ptr(self):
+            return A16
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return 1
+
+    with pytest.raises(ValueError, match="a holds"):
+        g.nvfp4_gemv(Fake(10), Fake(128), Fake(2048), Fake(16), Fake(256), 128, 256, 1, "plain")

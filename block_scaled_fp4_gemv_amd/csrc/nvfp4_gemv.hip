@@ -5,25 +5,37 @@
 // the four decoded operands, float32 accumulation, float16 cast.)
 //
 // With N = 1 this is a stream over A (8/9 of the bytes) and SFA (1/9): HBM
-// bound, not a dense contraction, so it runs on the vector ALUs:
-//   * Each workgroup owns `rows_per_wg` output rows of one batch and one K-slice.
-//     It first converts its K-slice of B into b'[k] = e2m1(B[k]) * e4m3(SFB[k/16])
-//     as float16 in LDS (exact: at most 6 significant bits, 2^-10 <= |b'| <= 2688).
-//   * A 16-byte chunk of A (32 elements, two scale blocks) is the unit of work of
-//     one lane. `LPR` lanes share a row and walk its K-slice in passes of LPR
-//     consecutive chunks, so a group's loads are contiguous 16-byte vectors.
-//   * Decode: v_cvt_scalef32_pk_f16_fp4 turns one byte (two E2M1 codes) into two
-//     float16 values; v_dot2_f32_f16 multiplies them with two b' values and
-//     accumulates in float32. Sums over one 16-element block are exact in float32
-//     (they are multiples of sfb/4 below 2^12 * sfb), then one FMA applies the
-//     SFA scale (decoded with v_cvt_pk_f32_fp8).
-//   * The lanes of a row are reduced with cross-lane shuffles; a float16 result
-//     is written, or for K-split problems a float32 partial, and the last
-//     workgroup of a row tile (atomic ticket) sums the partials in slice order.
-//   * Workgroup ids are remapped so that each XCD (own L2) gets a contiguous
-//     range of row tiles: blocked-layout scale lines are shared by rows r, r+32,
-//     r+64, r+96 of a 128-row block, which then stay in one L2.
-//   * The batch index is part of the grid: one launch covers all L.
+// bound, not a dense contraction, so it runs on the vector ALUs.
+//
+// Work split. A "chunk" is 16 bytes of A: 32 elements, two scale blocks. A
+// "slot" is one 16-byte line of the 128x4 blocked scale layout (submission
+// 69953 `to_blocked_batch`): slot s of a batch holds, for every group of four
+// scale blocks, the scales of the four rows 128*(s/32) + 32*i4 + s%32,
+// i4 = 0..3. Each workgroup owns a contiguous range of slots of one batch,
+// i.e. 4 rows per slot, and one K-slice. With that row set the workgroup's
+// blocked scales are whole 16-byte vectors, read once, coalesced, into LDS;
+// plain scales are staged the same way, so both layouts run the same
+// arithmetic and give bit-identical results.
+//
+// Inside a workgroup, LPR lanes share a row; lane j of a row group owns the
+// chunks j, j+LPR, j+2*LPR, j+3*LPR of every K-segment (4*LPR chunks), so each
+// wave-wide load is a contiguous run of 16-byte vectors. The lane converts its
+// four chunks of B into b'[k] = e2m1(B[k]) * e4m3(SFB[k/16]) once (float16 in
+// registers: exact, at most 6 significant bits, 2^-10 <= |b'| <= 2688) and
+// reuses them for every row. Per chunk and row:
+//   * v_cvt_scalef32_pk_f16_fp4 turns each byte (two E2M1 codes) into two
+//     float16 values, v_dot2_f32_f16 multiplies them with two b' values and
+//     accumulates in float32; sums over one 16-element block are exact in
+//     float32 (multiples of sfb/4 below 2^12 * sfb);
+//   * one FMA per block applies the SFA scale (v_cvt_pk_f32_fp8 decode).
+// Rows follow each other without a break: the loads of the next kPrefetch
+// chunk-steps are always in flight. A row's lanes are summed with DPP and the
+// per-wave sums are added in LDS in a fixed order; the result is rounded to
+// float16 once. K-split shapes (small M*L) write float32 partials and the last
+// workgroup of a row range (atomic ticket) adds them in slice order.
+//
+// Workgroup ids are remapped so that each XCD (own L2) gets a contiguous range
+// of slots; the batch index is part of the grid, so one launch covers all L.
 
 #include <hip/hip_runtime.h>
 
@@ -43,21 +55,35 @@ typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 2;                  // rows per lane group
-constexpr int kPrefetch = 4;              // passes of A kept in flight per lane
-constexpr int kMaxChunksPerWG = 512;      // b' segment in LDS: 512 chunks = 16384 k = 32 KiB
-constexpr int64_t kTargetWGs = 512;       // split K until the grid reaches ~2 WGs per CU
+constexpr int kCpl = 4;                   // chunks per lane per K-segment
+constexpr int kPrefetch = 8;              // chunk loads in flight per lane (multiple of kCpl)
+constexpr int kMaxLpr = 256;              // lanes per row, at most the whole workgroup
+constexpr int kSfaLdsBudget = 48 * 1024;  // staged scale bytes per workgroup
+constexpr int kStageMax = 12;             // 16-byte scale loads per thread (budget / 16 / threads)
+constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
 constexpr int kXcds = 8;                  // MI355X: 8 XCDs, WG ids dealt round-robin
+constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
+constexpr int kCachePolicyNT = 2;         // buffer load cache policy: non-temporal
+constexpr int64_t kMaxK = INT64_C(1) << 22; // keeps one workgroup's A offsets below 2^31
+
+static_assert(kPrefetch % kCpl == 0, "a row's chunk-steps must not straddle the prefetch ring");
+static_assert(kStageMax * kThreads * 16 >= kSfaLdsBudget, "staging registers cover the LDS budget");
 
 struct Params {
     int32_t M, K, L;
     int32_t S;            // K-slices
-    int32_t kc_split;     // 32-element chunks per K-slice
-    int32_t n_row_tiles;
+    int32_t kc_split;     // chunks per K-slice
+    int32_t P;            // workgroups per (batch, slice)
+    int32_t spw;          // slots per workgroup
+    int32_t ns;           // slots per batch that hold at least one row
+    int32_t segb;         // LDS bytes per row of staged scales
+    int32_t wide_plain;   // plain scales staged in 16-byte units
     int64_t sfa_batch;    // bytes per batch of SFA
     int64_t sfb_batch;    // bytes per batch of SFB
+    int64_t a_bytes;      // bytes of A (all batches)
+    uint32_t *counters;   // tickets [L][P] when S > 1
     float *partials;      // [L*M][S] when S > 1
-    uint32_t *counters;   // tickets [L][n_row_tiles] when S > 1
 };
 
 // Contiguous logical ids per XCD: hardware id i runs on XCD i % 8.
@@ -68,25 +94,21 @@ __device__ inline uint32_t xcd_remap(uint32_t i, uint32_t n)
     return x * q + min(x, r) + j;
 }
 
-// Byte offset of scale (row r, block kb) inside one batch of the scale matrix.
-// Blocked: the 128x4 tiling of submission 69953 `to_blocked_batch` (tile
-// (r/128, kb/4) of 512 bytes; inside it row r%32 selects a 16-byte line, and
-// (r%128)/32 and kb%4 the byte within it).
-template <int LAYOUT>
-__device__ inline int64_t sf_row_offset(int64_t r, int32_t nkb, int32_t ncb)
+// Row of local row q of a workgroup whose first slot is slot0: slot
+// slot0 + q/4, sub-row q%4 (the 32-row group inside the 128-row block).
+__device__ inline int32_t slot_row(int32_t slot0, int32_t q)
 {
-    if (LAYOUT == NVFP4_SF_PLAIN)
-        return r * nkb;
-    return (r >> 7) * (int64_t)ncb * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4;
+    const int32_t s = slot0 + (q >> 2);
+    return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31);
 }
 
-// Offset of the two scales of chunk c (blocks 2c and 2c+1) relative to the row.
+// Byte offset of the two scales of chunk c (blocks 2c, 2c+1) of row r.
 template <int LAYOUT>
-__device__ inline int32_t sf_chunk_offset(int32_t c)
+__device__ inline int64_t sf_pair_offset(int64_t r, int32_t c, int32_t nkb, int32_t ncb)
 {
     if (LAYOUT == NVFP4_SF_PLAIN)
-        return 2 * c;
-    return (c >> 1) * 512 + (c & 1) * 2;
+        return r * nkb + 2 * c;
+    return ((r >> 7) * ncb + (c >> 1)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 1) * 2;
 }
 
 // Reinterpretation helpers. They take their operand by value on purpose:
@@ -99,6 +121,20 @@ __device__ __attribute__((always_inline)) inline half2_t as_h2(uint32_t v)
 __device__ __attribute__((always_inline)) inline uint32_t as_u32(half2_t v)
 {
     return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __attribute__((always_inline)) inline float as_f32(int v)
+{
+    return __builtin_bit_cast(float, v);
+}
+__device__ __attribute__((always_inline)) inline int as_i32(float v)
+{
+    return __builtin_bit_cast(int, v);
+}
+
+// 16 bytes of A, streamed once: non-temporal
+__device__ __attribute__((always_inline)) inline uint4_t load_a(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNT);
 }
 
 // two E2M1 codes (byte SEL of w, low nibble first) -> two float16 values
@@ -114,26 +150,32 @@ __device__ __attribute__((always_inline)) inline uint16_t f16_bits(float v)
     return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-template <int LPR>
-__device__ inline float group_sum(float v)
+// Sum over aligned groups of RED lanes (RED = 1..64, a power of two) with DPP.
+// The group's sum ends in its last lane: row_shr accumulates a window of RED
+// lanes inside each 16-lane row, row_bcast15 / row_bcast31 carry the row sums
+// across rows.
+template <int RED>
+__device__ __attribute__((always_inline)) inline float group_sum(float v)
 {
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, 64);
+    if (RED >= 2)
+        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x111, 0xF, 0xF, true));  // row_shr:1
+    if (RED >= 4)
+        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x112, 0xF, 0xF, true));  // row_shr:2
+    if (RED >= 8)
+        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x114, 0xF, 0xF, true));  // row_shr:4
+    if (RED >= 16)
+        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x118, 0xF, 0xF, true));  // row_shr:8
+    if (RED >= 32)
+        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x142, 0xA, 0xF, false)); // row_bcast:15
+    if (RED >= 64)
+        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x143, 0xC, 0xF, false)); // row_bcast:31
     return v;
-}
-
-// LDS slot (16-byte units) of piece q (elements 8q..8q+7) of chunk ci. Pieces
-// with the same q of 64 consecutive chunks are contiguous, so a pass's reads
-// (consecutive lanes, consecutive chunks, same q) hit distinct banks.
-__device__ inline int lds_slot(int ci, int q)
-{
-    return ((ci >> 6) << 8) + (q << 6) + (ci & 63);
 }
 
 // Sum over one 16-element scale block: dwords w0, w1 of A (8 codes each)
 // against b' pieces b0, b1 (8 float16 each). Exact in float32 (see above).
-__device__ inline float dot_block(uint32_t w0, uint32_t w1, const uint4_t &b0, const uint4_t &b1)
+__device__ __attribute__((always_inline)) inline float dot_block(uint32_t w0, uint32_t w1,
+                                                                 const uint4_t &b0, const uint4_t &b1)
 {
     float s = 0.0f;
     s = __builtin_amdgcn_fdot2(fp4x2<0>(w0), as_h2(b0.x), s, false);
@@ -147,162 +189,241 @@ __device__ inline float dot_block(uint32_t w0, uint32_t w1, const uint4_t &b0, c
     return s;
 }
 
+// b' of one chunk: 16 bytes of packed B (32 codes) times its two SFB scales.
+__device__ __attribute__((always_inline)) inline void make_bprime(uint4_t b, uint32_t sfb2,
+                                                                  uint4_t (&out)[4])
+{
+    const half2_t sf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sfb2, 1.0f, false);
+    const half2_t s0 = {sf.x, sf.x}, s1 = {sf.y, sf.y};
+    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const half2_t sc = d < 2 ? s0 : s1;
+        out[d] = {as_u32(fp4x2<0>(w[d]) * sc), as_u32(fp4x2<1>(w[d]) * sc),
+                  as_u32(fp4x2<2>(w[d]) * sc), as_u32(fp4x2<3>(w[d]) * sc)};
+    }
+}
+
 template <int LAYOUT, int LPR, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
     uint16_t *__restrict__ C, Params p)
 {
-    constexpr int G = 64 / LPR;                  // row groups per wave
-    constexpr int ROWS_WG = kWaves * G * kRows;
-    constexpr int kStage = kMaxChunksPerWG * 4 / kThreads;   // b' pieces per thread
-    extern __shared__ uint4_t lds_b[];           // b' as float16, see lds_slot
+    constexpr int SEG = LPR * kCpl;              // chunks per K-segment
+    constexpr int G = kThreads / LPR;            // row groups (rows in flight) per workgroup
+    constexpr int WPG = LPR > 64 ? LPR / 64 : 1; // waves per row group
+    constexpr int RED = LPR < 64 ? LPR : 64;     // lanes summed inside one wave
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
     const int32_t s = (int32_t)(lid % (uint32_t)p.S);
     const uint32_t t2 = lid / (uint32_t)p.S;
-    const int32_t tile = (int32_t)(t2 % (uint32_t)p.n_row_tiles);
-    const int32_t l = (int32_t)(t2 / (uint32_t)p.n_row_tiles);
+    const int32_t tile = (int32_t)(t2 % (uint32_t)p.P);
+    const int32_t l = (int32_t)(t2 / (uint32_t)p.P);
 
-    const int32_t M = p.M, K = p.K;
+    const int32_t M = p.M, K = p.K, segb = p.segb;
     const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
-    const int32_t c_begin = s * p.kc_split;                  // this WG's K-slice, in chunks
+    const int32_t slot0 = tile * p.spw;
+    const int32_t nslots = min(p.spw, p.ns - slot0);
+    const int32_t nq = 4 * nslots;                        // local rows (some may be >= M)
+    const int32_t c_begin = s * p.kc_split;
     const int32_t c_end = min(c_begin + p.kc_split, nchunks);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int grp = lane / LPR, j = lane % LPR;
+    const int tid = threadIdx.x;
+    const int grp = tid / LPR, j = tid % LPR;
+    const int lane = tid & 63;
+    const int wig = WPG > 1 ? j >> 6 : 0;                 // wave index inside the row group
+    const bool leader = (lane % RED) == RED - 1;           // holds the group sum after group_sum
 
-    // ---- rows of this lane group; rows past M are clamped and not stored
-    int32_t row[kRows];
-    const uint8_t *arow[kRows];
-    const uint8_t *srow[kRows];
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-        const int32_t r = tile * ROWS_WG + (wave * G + grp) * kRows + i;
-        row[i] = r;
-        const int64_t rc = min(r, M - 1);
-        arow[i] = A + ((int64_t)l * M + rc) * (K >> 1);
-        srow[i] = SFA + (int64_t)l * p.sfa_batch + sf_row_offset<LAYOUT>(rc, nkb, ncb);
-    }
-    const uint8_t *brow = B + (int64_t)l * (K >> 1);
-    const uint8_t *sfbrow = SFB + (int64_t)l * p.sfb_batch;
+    const int64_t abatch = (int64_t)l * M;
+    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
+    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+    const uint8_t *b_l = B + (int64_t)l * (K >> 1);
+    float *part = (float *)(lds + (size_t)nq * segb);      // [nq][WPG] per-wave row sums
 
-    float acc[kRows];
-#pragma unroll
-    for (int i = 0; i < kRows; ++i)
-        acc[i] = 0.0f;
+    // A through a buffer resource based at the first row of this workgroup's
+    // first 128-row block: 32-bit lane offsets (the rows of one workgroup lie
+    // within a few blocks), and lanes past the end of A read zero.
+    const int32_t row_base = (slot0 >> 5) << 7;
+    const int64_t a_begin = (abatch + row_base) * (int64_t)(K >> 1);
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + a_begin), (short)0, (int)min(p.a_bytes - a_begin, (int64_t)0x7FFFFFFF),
+        kBufferFlags);
 
-    // The K-slice is walked in segments of at most kMaxChunksPerWG chunks, the
-    // b' capacity of LDS (one segment unless K > 16384).
-    for (int32_t c0 = c_begin; c0 < c_end; c0 += kMaxChunksPerWG) {
-        const int32_t nck = min(kMaxChunksPerWG, c_end - c0);
-        const int32_t npass = (nck + LPR - 1) / LPR;
-        if (c0 != c_begin)
-            __syncthreads();             // the previous segment's b' reads are done
+    const int32_t NR = (nq + G - 1) / G;                   // row rounds per group
+    const int32_t nsteps = NR * kCpl;                      // one step = one chunk of one row
 
-        // ---- loads first, in this order: B and SFB for the b' staging, then
-        // the first kPrefetch passes of A. Vector loads return in order, so
-        // the staging waits only for its own (L2-resident) loads while A is in
-        // flight. Every load is issued unconditionally (clamped to a valid
-        // element) so that the wait counts stay exact; only real pieces are used.
-        uint32_t bw[kStage], bs[kStage];
-#pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int pc = min(threadIdx.x + i * kThreads, nck * 4 - 1);   // piece = 8 elements
-            const int32_t kb = 2 * (c0 + (pc >> 2)) + ((pc & 3) >> 1);
-            bw[i] = *(const uint32_t *)(brow + (int64_t)(c0 * 4 + pc) * 4);
-            bs[i] = sfbrow[LAYOUT == NVFP4_SF_PLAIN ? kb : (kb >> 2) * 512 + (kb & 3)];
-        }
+    for (int32_t c0 = c_begin; c0 < c_end; c0 += SEG) {
+        const int32_t nck = min(SEG, c_end - c0);
+        const bool first = c0 == c_begin;
+        if (!first)
+            __syncthreads();                               // previous segment's LDS reads done
 
-        uint4_t abuf[kPrefetch][kRows];
-        uint32_t sbuf[kPrefetch][kRows];
-        auto load_pass = [&](int pass, uint4_t (&av)[kRows], uint32_t (&sv)[kRows]) {
-            const int32_t ci = c0 + min(pass * LPR + j, nck - 1);
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                av[i] = __builtin_nontemporal_load((const uint4_t *)(arow[i] + (int64_t)ci * 16));
-                sv[i] = *(const uint16_t *)(srow[i] + sf_chunk_offset<LAYOUT>(ci));
-            }
+        // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
+        // the end read a clamped (valid) chunk so that every load is
+        // unconditional and the wait counts stay exact.
+        auto a_off = [&](int32_t t) -> uint32_t {
+            const int32_t q = min(grp + G * (t / kCpl), nq - 1);
+            const int32_t r = min(slot_row(slot0, q), M - 1);
+            const int32_t ci = c0 + min(j + (t % kCpl) * LPR, nck - 1);
+            return (uint32_t)(r - row_base) * (uint32_t)(K >> 1) + (uint32_t)ci * 16u;
         };
+        uint4_t abuf[kPrefetch];
+        uint4_t bload[kCpl];
+        uint32_t sload[kCpl];
+        auto load_bprime_and_a = [&]() {
 #pragma unroll
-        for (int u = 0; u < kPrefetch; ++u)
-            load_pass(u, abuf[u], sbuf[u]);     // passes past the end load a clamped chunk
+            for (int k = 0; k < kCpl; ++k) {
+                const int32_t ci = c0 + min(j + k * LPR, nck - 1);
+                bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
+                sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kPrefetch; ++u)
+                abuf[u] = load_a(arsrc, a_off(u));
+            __builtin_amdgcn_sched_barrier(0);
+        };
 
-        // ---- stage b' = e2m1(B) * e4m3(SFB) for this segment into LDS
+        // Loads are issued in this order: scales to stage, B for b', then the
+        // first kPrefetch steps of A. Vector loads complete in order, so the
+        // staging and the b' decode wait only for their own loads while A is
+        // still in flight.
+        // ---- scales of this workgroup's rows and segment -> LDS, layout [q][block]
+        if (LAYOUT == NVFP4_SF_BLOCKED) {
+            // item (slot, 4-block group): one 16-byte vector = 4 rows x 4 blocks
+            const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1;
+            const int32_t items = nslots * ncb_seg;
+            uint4_t v[kStageMax];
 #pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int pc = threadIdx.x + i * kThreads;
-            if (pc < nck * 4) {
-                const half2_t sf2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[i], 1.0f, false);
-                const half2_t sfv = {sf2.x, sf2.x};
-                uint4_t v;
-                v.x = as_u32(fp4x2<0>(bw[i]) * sfv);
-                v.y = as_u32(fp4x2<1>(bw[i]) * sfv);
-                v.z = as_u32(fp4x2<2>(bw[i]) * sfv);
-                v.w = as_u32(fp4x2<3>(bw[i]) * sfv);
-                lds_b[lds_slot(pc >> 2, pc & 3)] = v;
+            for (int i = 0; i < kStageMax; ++i) {
+                const int32_t it = min(tid + i * kThreads, items - 1);
+                const int32_t sl = it % nslots, cb = it / nslots, sg = slot0 + sl;
+                v[i] = *(const uint4_t *)(sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16);
+            }
+            load_bprime_and_a();
+            // items past the end repeat the last item: same bytes, same place
+#pragma unroll
+            for (int i = 0; i < kStageMax; ++i) {
+                const int32_t it = min(tid + i * kThreads, items - 1);
+                const int32_t sl = it % nslots, cb = it / nslots;
+                uint8_t *dst = lds + (size_t)(sl * 4) * segb + cb * 4;
+                *(uint32_t *)(dst) = v[i].x;
+                *(uint32_t *)(dst + segb) = v[i].y;
+                *(uint32_t *)(dst + 2 * segb) = v[i].z;
+                *(uint32_t *)(dst + 3 * segb) = v[i].w;
+            }
+        } else if (p.wide_plain) {
+            // item (row, 8 chunks): 16 contiguous bytes of a plain scale row
+            const int32_t units = nck >> 3;                // nck % 8 == 0 on this path
+            const int32_t items = nq * units;
+            uint4_t v[kStageMax];
+#pragma unroll
+            for (int i = 0; i < kStageMax; ++i) {
+                const int32_t it = min(tid + i * kThreads, items - 1);
+                const int32_t q = it / units, u = it % units;
+                const int32_t r = min(slot_row(slot0, q), M - 1);
+                v[i] = *(const uint4_t *)(sfa_l + (int64_t)r * nkb + 2 * c0 + 16 * u);
+            }
+            load_bprime_and_a();
+#pragma unroll
+            for (int i = 0; i < kStageMax; ++i) {
+                const int32_t it = min(tid + i * kThreads, items - 1);
+                const int32_t q = it / units, u = it % units;
+                *(uint4_t *)(lds + (size_t)q * segb + 16 * u) = v[i];
+            }
+        } else {
+            // item (row, chunk): the two scales of one chunk
+            load_bprime_and_a();
+            for (int32_t it = tid; it < nq * nck; it += kThreads) {
+                const int32_t q = it / nck, c = it % nck;
+                const int32_t r = min(slot_row(slot0, q), M - 1);
+                *(uint16_t *)(lds + (size_t)q * segb + 2 * c) =
+                    *(const uint16_t *)(sfa_l + (int64_t)r * nkb + 2 * (c0 + c));
             }
         }
+
+        // ---- b' for this lane's chunks of the segment (registers, reused for every row)
+        uint4_t bp[kCpl][4];
+#pragma unroll
+        for (int k = 0; k < kCpl; ++k)
+            make_bprime(bload[k], sload[k], bp[k]);
         __syncthreads();
 
-        // ---- passes: no branches inside; passes past the end and lanes past
-        // the segment read a clamped (valid) chunk and their contribution is
-        // masked, so each pass waits only for its own data.
-        for (int p0 = 0; p0 < npass; p0 += kPrefetch) {
+        // ---- the group's rows one after another, kPrefetch chunk loads ahead
+        float acc = 0.0f;
+        for (int32_t t0 = 0; t0 < nsteps; t0 += kPrefetch) {
 #pragma unroll
             for (int u = 0; u < kPrefetch; ++u) {
-                const int pass = p0 + u;
-                const int32_t ci_raw = pass * LPR + j;
-                const bool live = ci_raw < nck;
-                const int32_t ci = min(ci_raw, nck - 1);
-                const uint4_t b0 = lds_b[lds_slot(ci, 0)];
-                const uint4_t b1 = lds_b[lds_slot(ci, 1)];
-                const uint4_t b2 = lds_b[lds_slot(ci, 2)];
-                const uint4_t b3 = lds_b[lds_slot(ci, 3)];
-#pragma unroll
-                for (int i = 0; i < kRows; ++i) {
-                    const uint4_t a = abuf[u][i];
-                    const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sbuf[u][i], false);
-                    const float lo = dot_block(a.x, a.y, b0, b1);
-                    const float hi = dot_block(a.z, a.w, b2, b3);
-                    const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc[i]));
-                    acc[i] = live ? nacc : acc[i];
+                const int k = u % kCpl;                    // t0 % kCpl == 0
+                const int32_t t = t0 + u;
+                const int32_t q = grp + G * (t / kCpl);
+                const int32_t qc = min(q, nq - 1);
+                const int32_t cl = j + k * LPR;            // chunk inside the segment
+                const uint32_t sv = *(const uint16_t *)(lds + (size_t)qc * segb + 2 * min(cl, nck - 1));
+                const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sv, false);
+                const uint4_t a = abuf[u];
+                const float lo = dot_block(a.x, a.y, bp[k][0], bp[k][1]);
+                const float hi = dot_block(a.z, a.w, bp[k][2], bp[k][3]);
+                const float base = k == 0 ? 0.0f : acc;
+                const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, base));
+                acc = cl < nck ? nacc : base;
+                // refill the slot only after its last use: a load hoisted above
+                // the use would need a second register set and copies that wait
+                __builtin_amdgcn_sched_barrier(0);
+                abuf[u] = load_a(arsrc, a_off(t + kPrefetch));
+                if (k == kCpl - 1) {
+                    const float v = group_sum<RED>(acc);
+                    if (leader && q < nq) {
+                        float *dst = part + q * WPG + wig;
+                        *dst = first ? v : *dst + v;
+                    }
                 }
-                load_pass(pass + kPrefetch, abuf[u], sbuf[u]);
             }
         }
     }
+    __syncthreads();
 
-    // ---- reduce the LPR lanes of each row group and store
-#pragma unroll
-    for (int i = 0; i < kRows; ++i)
-        acc[i] = group_sum<LPR>(acc[i]);
-
+    // ---- per-row totals: add the per-wave sums in a fixed order, round once
     if (!SPLIT) {
-        if (j == 0) {
+        for (int32_t q = tid; q < nq; q += kThreads) {
+            const int32_t r = slot_row(slot0, q);
+            if (r < M) {
+                float v = part[q * WPG];
 #pragma unroll
-            for (int i = 0; i < kRows; ++i)
-                if (row[i] < M)
-                    C[(int64_t)l * M + row[i]] = f16_bits(acc[i]);
+                for (int w = 1; w < WPG; ++w)
+                    v += part[q * WPG + w];
+                C[abatch + r] = f16_bits(v);
+            }
         }
         return;
     }
 
-    // ---- K-split: float32 partial per (row, slice); the last WG of the tile
-    // (atomic ticket) sums the partials in slice order and resets the ticket.
-    if (j == 0) {
+    // ---- K-split: float32 partial per (row, slice); the last workgroup of the
+    // row range (atomic ticket) adds the partials in slice order and resets the
+    // ticket. Partials are written and read with agent-scope atomic stores and
+    // loads, which are coherent across the XCDs without any cache maintenance,
+    // so the handshake only needs the stores to have completed before the
+    // ticket is taken. Agent-scope fences are avoided on purpose: on this chip
+    // they write back and invalidate the whole L2 of the XCD, once per workgroup.
+    for (int32_t q = tid; q < nq; q += kThreads) {
+        const int32_t r = slot_row(slot0, q);
+        if (r < M) {
+            float v = part[q * WPG];
 #pragma unroll
-        for (int i = 0; i < kRows; ++i)
-            if (row[i] < M)
-                __hip_atomic_store(&p.partials[((int64_t)l * M + row[i]) * p.S + s], acc[i],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int w = 1; w < WPG; ++w)
+                v += part[q * WPG + w];
+            __hip_atomic_store(&p.partials[(abatch + r) * p.S + s], v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __shared__ uint32_t is_last;
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);     // this wave's partial stores are done
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t *ctr = &p.counters[(int64_t)l * p.n_row_tiles + tile];
-        const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        uint32_t *ctr = &p.counters[(int64_t)l * p.P + tile];
+        const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = prev == (uint32_t)(p.S - 1);
         if (last)
             __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -311,16 +432,15 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     __syncthreads();
     if (!is_last)
         return;
-    __threadfence();
-    for (int t = threadIdx.x; t < ROWS_WG; t += kThreads) {
-        const int32_t r = tile * ROWS_WG + t;
-        if (r >= M)
-            break;
-        const float *part = p.partials + ((int64_t)l * M + r) * p.S;
-        float v = 0.0f;
-        for (int k = 0; k < p.S; ++k)
-            v += __hip_atomic_load(part + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        C[(int64_t)l * M + r] = f16_bits(v);
+    for (int32_t q = tid; q < nq; q += kThreads) {
+        const int32_t r = slot_row(slot0, q);
+        if (r < M) {
+            const float *pp = p.partials + (abatch + r) * p.S;
+            float v = 0.0f;
+            for (int k = 0; k < p.S; ++k)
+                v += __hip_atomic_load(pp + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            C[abatch + r] = f16_bits(v);
+        }
     }
 }
 
@@ -328,10 +448,13 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
 
 struct Plan {
     int lpr;
-    int rows_wg;
     int S;
-    int kc_split;         // chunks per slice
-    int n_row_tiles;
+    int kc_split;         // chunks per K-slice
+    int P;                // workgroups per (batch, slice)
+    int spw;              // slots per workgroup
+    int ns;               // slots per batch
+    int segb;             // LDS bytes per staged scale row
+    int wide_plain;
     int64_t n_wg;
     int lds_bytes;
     size_t ws_partials;   // bytes of float32 partials (after the ticket region)
@@ -350,19 +473,32 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int choose_lpr(int64_t nchunks)
+int pow2_ceil(int64_t v)
 {
-    if (nchunks >= 64)
-        return (nchunks % 64 == 0 || nchunks % 32 != 0) ? 64 : 32;
-    int v = 1;
-    while (v < nchunks)
-        v <<= 1;
-    return v;
+    int p = 1;
+    while (p < v)
+        p <<= 1;
+    return p;
+}
+
+// Lanes per row for a K-slice of nc chunks: kCpl chunks per lane, the whole
+// workgroup at most (longer slices are walked in segments of kCpl*256 chunks).
+int choose_lpr(int64_t nc)
+{
+    return std::min<int>(kMaxLpr, pow2_ceil(cdiv(nc, kCpl)));
+}
+
+// LDS bytes per staged scale row: 2 bytes per chunk of the segment, padded so
+// that the rows read together by the groups of one wave start on other banks.
+int seg_bytes(int lpr)
+{
+    const int raw = 2 * kCpl * lpr + (lpr < 64 ? 2 * lpr : 0);
+    return (int)align_up((size_t)raw, 16);
 }
 
 nvfp4_status_t check_shape(int64_t M, int64_t K, int64_t L)
 {
-    if (M < 1 || K < 32 || L < 1 || K % 32 != 0)
+    if (M < 1 || K < 32 || L < 1 || K % 32 != 0 || K > kMaxK)
         return NVFP4_ERR_INVALID_SHAPE;
     // int32 indices in the kernel; byte sizes well inside int64
     if (M > INT32_MAX / 2 || K > INT32_MAX / 2 || L > INT32_MAX / 2 || M * L > INT32_MAX / 2)
@@ -376,20 +512,32 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
 {
     Plan pl{};
     const int64_t nchunks = K / 32;
-    pl.lpr = choose_lpr(nchunks);
-    pl.rows_wg = kWaves * (64 / pl.lpr) * kRows;
-    pl.n_row_tiles = (int)cdiv(M, pl.rows_wg);
-    const int64_t base = (int64_t)pl.n_row_tiles * L;
-    // Split K only to fill the machine: S > 1 implies base < kTargetWGs, which
-    // bounds the number of tickets. Each slice keeps at least one full pass.
-    const int64_t s_max = std::max<int64_t>(1, nchunks / pl.lpr);
-    int64_t S = std::min<int64_t>(cdiv(kTargetWGs, base), s_max);
-    int64_t kc = cdiv(cdiv(nchunks, S), pl.lpr) * pl.lpr;
+    // slots holding at least one row: full 128-row blocks have 32, the last one min(32, M % 128)
+    pl.ns = (int)(32 * (M / 128) + std::min<int64_t>(32, M % 128));
+    const int64_t total_slots = L * pl.ns;
+
+    int64_t S = 1;
+    if (total_slots < kTargetWGs) {
+        // too few rows to fill the machine: split K, keeping >= 256 chunks per
+        // slice so that one slot (4 rows) still occupies every lane
+        S = std::max<int64_t>(1, std::min<int64_t>(kTargetWGs / total_slots, nchunks / 256));
+    }
+    const int64_t kc = cdiv(nchunks, S);
     S = cdiv(nchunks, kc);
     pl.S = (int)S;
     pl.kc_split = (int)kc;
-    pl.n_wg = base * S;
-    pl.lds_bytes = (int)(cdiv(std::min<int64_t>(kc, kMaxChunksPerWG), 64) * 64 * 4 * 16);
+    pl.lpr = choose_lpr(kc);
+    pl.segb = seg_bytes(pl.lpr);
+
+    const int64_t spw_max = std::max<int64_t>(1, kSfaLdsBudget / (4 * pl.segb));
+    int64_t spw = total_slots >= kTargetWGs ? cdiv(total_slots, kTargetWGs) : 1;
+    spw = std::min(spw, spw_max);
+    pl.spw = (int)spw;
+    pl.P = (int)cdiv(pl.ns, spw);
+    pl.n_wg = (int64_t)pl.P * L * S;
+    const int wpg = pl.lpr > 64 ? pl.lpr / 64 : 1;
+    pl.lds_bytes = (int)(4 * spw * pl.segb + 4 * spw * wpg * (int)sizeof(float));
+    pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
     if (S > 1) {
         pl.ws_partials = align_up((size_t)(L * M * S) * sizeof(float), kWsAlign);
         pl.ws_total = kCounterBytes + pl.ws_partials;
@@ -420,6 +568,8 @@ hipError_t launch_layout(const Plan &pl, const void *a, const void *b, const voi
                          void *c, const Params &p, hipStream_t st)
 {
     switch (pl.lpr) {
+    case 256: return launch_lpr<LAYOUT, 256>(pl, a, b, sfa, sfb, c, p, st);
+    case 128: return launch_lpr<LAYOUT, 128>(pl, a, b, sfa, sfb, c, p, st);
     case 64: return launch_lpr<LAYOUT, 64>(pl, a, b, sfa, sfb, c, p, st);
     case 32: return launch_lpr<LAYOUT, 32>(pl, a, b, sfa, sfb, c, p, st);
     case 16: return launch_lpr<LAYOUT, 16>(pl, a, b, sfa, sfb, c, p, st);
@@ -442,7 +592,7 @@ nvfp4_status_t validate(const void *a, const void *b, const void *sfa, const voi
         return st;
     if (sf_layout != NVFP4_SF_PLAIN && sf_layout != NVFP4_SF_BLOCKED)
         return NVFP4_ERR_INVALID_LAYOUT;
-    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(c, 2))
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sfa, 16) || !aligned(sfb, 4) || !aligned(c, 2))
         return NVFP4_ERR_MISALIGNED;
     return NVFP4_OK;
 }
@@ -457,7 +607,12 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
     p.L = (int32_t)L;
     p.S = pl.S;
     p.kc_split = pl.kc_split;
-    p.n_row_tiles = pl.n_row_tiles;
+    p.P = pl.P;
+    p.spw = pl.spw;
+    p.ns = pl.ns;
+    p.segb = pl.segb;
+    p.wide_plain = pl.wide_plain;
+    p.a_bytes = L * M * (K / 2);
     const int64_t nkb = K / 16, ncb = cdiv(nkb, 4);
     if (sf_layout == NVFP4_SF_PLAIN) {
         p.sfa_batch = M * nkb;
@@ -575,7 +730,7 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
         return st;
     const Plan pl = make_plan(M, K, L);
     plan->lanes_per_row = pl.lpr;
-    plan->rows_per_wg = pl.rows_wg;
+    plan->rows_per_wg = 4 * pl.spw;
     plan->k_splits = pl.S;
     plan->k_per_split = pl.kc_split * 32;
     plan->workgroups = pl.n_wg;
@@ -590,7 +745,7 @@ const char *nvfp4_status_string(int status)
     case NVFP4_OK: return "success";
     case NVFP4_ERR_NULL_POINTER: return "a required pointer is NULL";
     case NVFP4_ERR_INVALID_SHAPE: return "invalid shape (need M, K, L >= 1, K % 32 == 0, sizes in range)";
-    case NVFP4_ERR_MISALIGNED: return "misaligned pointer (a, b: 16 B; sfa, sfb: 4 B; c: 2 B)";
+    case NVFP4_ERR_MISALIGNED: return "misaligned pointer (a, b, sfa: 16 B; sfb: 4 B; c: 2 B)";
     case NVFP4_ERR_INVALID_LAYOUT: return "invalid scale layout";
     case NVFP4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case NVFP4_ERR_HIP: return "HIP runtime error";

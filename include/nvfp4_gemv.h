@@ -42,8 +42,8 @@
  *     the stream.
  *   - Every argument is validated before any HIP call; on failure nothing is
  *     launched and a nonzero nvfp4_status_t is returned.
- *   - Requirements: M, K, L >= 1; K % 32 == 0; L*M*K/2 < 2^62; a and b 16-byte
- *     aligned; sfa and sfb 4-byte aligned; c 2-byte aligned.
+ *   - Requirements: M, K, L >= 1; K % 32 == 0; L*M*K/2 < 2^62; a, b and sfa
+ *     16-byte aligned; sfb 4-byte aligned; c 2-byte aligned.
  */
 #ifndef NVFP4_GEMV_H
 #define NVFP4_GEMV_H
@@ -103,8 +103,8 @@ nvfp4_status_t nvfp4_gemv_ex(const void *a, const void *b, const void *sfa, cons
 /*
  * Launch plan chosen for a shape (for tests and reports). Returns NVFP4_OK and
  * fills the fields, or an error status for an invalid shape.
- *   lanes_per_row  lanes that share one output row (1..64)
- *   rows_per_wg    output rows per workgroup
+ *   lanes_per_row  lanes that share one output row (1..256)
+ *   rows_per_wg    output rows per workgroup (at most; 4 per 16-byte scale slot)
  *   k_splits       number of K-slices (1 = no split)
  *   k_per_split    K-elements per slice
  *   workgroups     grid size; threads_per_wg threads each

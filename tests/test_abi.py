@@ -55,15 +55,15 @@ def test_bad_shapes(M, K, L):
     assert call(M=M, K=K, L=L) == g.NVFP4_ERR_INVALID_SHAPE
 
 
-@pytest.mark.parametrize("ptr,off", [("a", 8), ("b", 4), ("sfa", 2), ("sfb", 1), ("c", 1)])
+@pytest.mark.parametrize("ptr,off", [("a", 8), ("b", 4), ("sfa", 4), ("sfa", 8), ("sfb", 1), ("sfb", 2), ("c", 1)])
 def test_misaligned(ptr, off):
     assert call(**{ptr: OK_ARGS[ptr] + off}) == g.NVFP4_ERR_MISALIGNED
 
 
 def test_alignment_minimums_accepted_by_validation():
-    # 4-byte aligned scales and 2-byte aligned c pass validation (they then
+    # 4-byte aligned sfb and 2-byte aligned c pass validation (they then
     # fail later only because there is no GPU here, never with MISALIGNED)
-    st = call(sfa=OK_ARGS["sfa"] + 4, sfb=OK_ARGS["sfb"] + 4, c=OK_ARGS["c"] + 2)
+    st = call(sfb=OK_ARGS["sfb"] + 4, c=OK_ARGS["c"] + 2)
     assert st not in (g.NVFP4_ERR_MISALIGNED, g.NVFP4_ERR_NULL_POINTER, g.NVFP4_ERR_INVALID_SHAPE)
 
 
@@ -96,34 +96,36 @@ def test_workspace_bytes():
 @pytest.mark.parametrize("w", synth.ALL, ids=lambda w: w.name)
 def test_plans(w):
     p = g.nvfp4_gemv_plan(w.M, w.K, w.L)
-    assert 1 <= p["lanes_per_row"] <= 64
+    assert 1 <= p["lanes_per_row"] <= 256
     assert p["k_splits"] >= 1
     assert p["k_per_split"] % 32 == 0
     assert p["k_splits"] * p["k_per_split"] >= w.K > (p["k_splits"] - 1) * p["k_per_split"]
-    tiles = synth.ceil_div(w.M, p["rows_per_wg"])
+    ns = 32 * (w.M // 128) + min(32, w.M % 128)
+    tiles = synth.ceil_div(ns, p["rows_per_wg"] // 4)
     assert p["workgroups"] == tiles * w.L * p["k_splits"]
-    assert p["lds_bytes"] <= 32 * 1024
+    assert p["lds_bytes"] <= 64 * 1024
     assert p["threads_per_wg"] == 256
 
 
 def test_long_k_is_segmented_not_split():
-    # K beyond the 16384-element LDS segment no longer forces a K-split
+    # K beyond one segment (4 chunks x 256 lanes) is walked in segments, not split
     p = g.nvfp4_gemv_plan(7168, 65536, 1)
-    assert p["k_splits"] == 1 and p["k_per_split"] == 65536 and p["lds_bytes"] == 32768
+    assert p["k_splits"] == 1 and p["k_per_split"] == 65536 and p["lanes_per_row"] == 256
 
 
 def test_split_only_for_small_grids():
     for M, K, L in [(127, 16384, 1), (1000, 4096, 3), (1, 32768, 1), (5, 65536, 2)]:
         p = g.nvfp4_gemv_plan(M, K, L)
-        tiles = synth.ceil_div(M, p["rows_per_wg"])
+        ns = 32 * (M // 128) + min(32, M % 128)
         if p["k_splits"] > 1:
-            assert tiles * L < 512
+            assert ns * L < 256 and p["k_per_split"] >= 256 * 32
             assert g.nvfp4_gemv_workspace_bytes(M, K, L) >= 4096
 
 
 def test_headline_plan_has_no_split():
     p = g.nvfp4_gemv_plan(7168, 16384, 1)
-    assert p["k_splits"] == 1 and p["lanes_per_row"] == 64
+    assert p["k_splits"] == 1 and p["lanes_per_row"] == 128
+    assert p["workgroups"] == 256 and p["rows_per_wg"] == 28
 
 
 def test_plan_rejects_bad_shape():

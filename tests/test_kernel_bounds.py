@@ -1,15 +1,18 @@
-"""CPU check that every address the GEMV kernel forms stays inside its buffers.
+"""CPU check of the GEMV kernel's address arithmetic, before it runs on a GPU.
 
-This mirrors the kernel's index arithmetic (nvfp4_gemv.hip) for the whole grid
-of each tested shape, using the launch plan the library reports, and checks:
-  * A, B, SFA, SFB reads are in bounds, and scale reads never touch the padding
-    of the blocked layout,
-  * every output row is written exactly once, by the right workgroup,
-  * LDS slots stay inside the dynamic LDS allocation,
-  * split-K partial and counter indices stay inside the workspace.
-It runs before any kernel change goes to the GPU. Keep it in step with the
-kernel's constants: kWaves = 4, kRows = 2, kPrefetch = 4, kStage = 8,
-kMaxChunksPerWG = 512 (LDS segment), 1024 tickets.
+This mirrors the index arithmetic of nvfp4_gemv.hip for the whole grid of each
+tested shape, using the launch plan the library reports, and checks:
+  * every A, B, SFA and SFB read is inside its buffer (A through a buffer
+    resource: inside the resource's byte range),
+  * the scales staged into LDS are exactly the ones the compute reads for every
+    real (row, chunk): the staging and the read side agree byte for byte, and
+    no real row reads padding of the blocked layout,
+  * every staging item is covered by the fixed number of loads per thread, and
+    LDS offsets stay inside the allocation,
+  * every output row is written exactly once, and split-K partial and ticket
+    indices stay inside the workspace.
+Keep it in step with the kernel's constants: 256 threads, 4 chunks per lane,
+8 chunk loads in flight, 12 staging loads per thread, 1024 tickets.
 """
 import numpy as np
 import pytest
@@ -17,9 +20,7 @@ import pytest
 import block_scaled_fp4_gemv_amd as g
 import synth
 
-K_WAVES, K_ROWS, K_PREFETCH, K_THREADS = 4, 2, 4, 256
-K_STAGE = 512 * 4 // K_THREADS
-XCDS = 8
+THREADS, CPL, PREFETCH, STAGE_MAX, XCDS = 256, 4, 8, 12, 8
 
 
 def cdiv(a, b):
@@ -32,107 +33,153 @@ def xcd_remap(i, n):
     return x * q + np.minimum(x, r) + j
 
 
-def sf_row_offset(layout, r, nkb, ncb):
+def slot_row(slot0, q):
+    s = slot0 + (q >> 2)
+    return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31)
+
+
+def seg_bytes(lpr):
+    raw = 2 * CPL * lpr + (2 * lpr if lpr < 64 else 0)
+    return cdiv(raw, 16) * 16
+
+
+def sf_offset(layout, r, kb, nkb, ncb):
+    """Byte of scale (row r, block kb) inside one batch (numpy-vectorised)."""
     if layout == 0:
-        return r * nkb
-    return (r >> 7) * ncb * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4
+        return r * nkb + kb
+    return ((r >> 7) * ncb + (kb >> 2)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (kb & 3)
 
 
-def sf_chunk_offset(layout, c):
-    if layout == 0:
-        return 2 * c
-    return (c >> 1) * 512 + (c & 1) * 2
-
-
-def lds_slot(ci, q):
-    return ((ci >> 6) << 8) + (q << 6) + (ci & 63)
-
-
-def check_shape(M, K, L, layout):
-    p = g.nvfp4_gemv_plan(M, K, L)
-    lpr, rows_wg, S, kc = p["lanes_per_row"], p["rows_per_wg"], p["k_splits"], p["k_per_split"] // 32
-    n_wg = p["workgroups"]
-    G = 64 // lpr
-    assert rows_wg == K_WAVES * G * K_ROWS
-    n_tiles = cdiv(M, rows_wg)
+def check_shape(M, K, L, layout, plan=None, workspace_bytes=None):
+    p = (plan or g.nvfp4_gemv_plan)(M, K, L)
+    ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
+    lpr, spw, S = p["lanes_per_row"], p["rows_per_wg"] // 4, p["k_splits"]
+    kc, n_wg, lds_bytes = p["k_per_split"] // 32, p["workgroups"], p["lds_bytes"]
+    assert p["threads_per_wg"] == THREADS
     nchunks, nkb = K // 32, K // 16
     ncb = cdiv(nkb, 4)
-    a_size, b_size = L * M * K // 2, L * K // 2
+    ns = 32 * (M // 128) + min(32, M % 128)
+    P = cdiv(ns, spw)
+    assert n_wg == P * L * S
+    SEG, G, WPG = lpr * CPL, THREADS // lpr, max(1, lpr // 64)
+    segb = seg_bytes(lpr)
+    assert lds_bytes == 4 * spw * segb + 4 * spw * WPG * 4
+    assert lds_bytes <= 64 * 1024
+    wide_plain = nchunks % 8 == 0 and kc % 8 == 0
+    a_bytes, b_size = L * M * K // 2, L * K // 2
     sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512
     sfb_batch = nkb if layout == 0 else ncb * 512
-    lds_slots = p["lds_bytes"] // 16
-
-    # valid (non-padding) scale bytes of one batch
-    valid_sfa = np.zeros(sfa_batch, bool)
+    valid_sfa = np.zeros(sfa_batch, bool)       # bytes that hold a real scale
     rr, kk = np.meshgrid(np.arange(M), np.arange(nkb), indexing="ij")
-    valid_sfa[sf_row_offset(layout, rr, nkb, ncb) + (kk if layout == 0 else (kk >> 2) * 512 + (kk & 3))] = True
+    valid_sfa[sf_offset(layout, rr, kk, nkb, ncb)] = True
     valid_sfb = np.zeros(sfb_batch, bool)
-    kb = np.arange(nkb)
-    valid_sfb[kb if layout == 0 else (kb >> 2) * 512 + (kb & 3)] = True
+    valid_sfb[sf_offset(layout, np.zeros(nkb, np.int64), np.arange(nkb), nkb, ncb)] = True
 
     written = np.zeros(L * M, np.int64)
     lids = xcd_remap(np.arange(n_wg), n_wg)
     assert np.array_equal(np.sort(lids), np.arange(n_wg)), "remap is not a bijection"
-    tid = np.arange(K_THREADS)
-    lane, wave = tid & 63, tid >> 6
-    grp, j = lane // lpr, lane % lpr
+    tid = np.arange(THREADS)
+    grp, j = tid // lpr, tid % lpr
     for lid in lids:
-        s = lid % S
-        t2 = lid // S
-        tile = t2 % n_tiles
-        l = t2 // n_tiles
+        s, t2 = lid % S, lid // S
+        tile, l = t2 % P, t2 // P
         assert l < L
-        c_begin = s * kc
-        c_end = min(c_begin + kc, nchunks)
+        slot0 = tile * spw
+        nslots = min(spw, ns - slot0)
+        assert nslots >= 1
+        nq = 4 * nslots
+        assert nq * segb + nq * WPG * 4 <= lds_bytes
+        c_begin, c_end = s * kc, min(s * kc + kc, nchunks)
         assert c_end > c_begin
-        for c0 in range(c_begin, c_end, 512):
-            nck = min(512, c_end - c0)
-            npass = cdiv(nck, lpr)
-            # staging loads (clamped pieces) and LDS writes (real pieces only)
-            for i in range(K_STAGE):
-                pc_raw = tid + i * K_THREADS
-                pc = np.minimum(pc_raw, nck * 4 - 1)
-                boff = l * (K // 2) + (c0 * 4 + pc) * 4
-                assert boff.min() >= 0 and (boff + 4).max() <= b_size
-                kbb = 2 * (c0 + (pc >> 2)) + ((pc & 3) >> 1)
-                so = kbb if layout == 0 else (kbb >> 2) * 512 + (kbb & 3)
-                assert so.max() < sfb_batch and valid_sfb[so].all()
-                real = pc_raw < nck * 4
-                slots = lds_slot(pc_raw[real] >> 2, pc_raw[real] & 3)
-                assert slots.size == 0 or slots.max() < lds_slots
-            # main-loop loads: passes run to a multiple of kPrefetch, plus the
-            # prefetch issued past the end
-            last_pass = cdiv(npass, K_PREFETCH) * K_PREFETCH + K_PREFETCH
-            for i in range(K_ROWS):
-                r = tile * rows_wg + (wave * G + grp) * K_ROWS + i
-                rc = np.minimum(r, M - 1)
-                abase = (l * M + rc) * (K // 2)
-                sbase = l * sfa_batch + sf_row_offset(layout, rc, nkb, ncb)
-                for pas in (0, 1, npass - 1, npass, last_pass - 1):
-                    ci = c0 + np.minimum(pas * lpr + j, nck - 1)
-                    ao = abase + ci * 16
-                    assert ao.min() >= 0 and (ao + 16).max() <= a_size
-                    so = sbase + sf_chunk_offset(layout, ci)
-                    assert (so + 2).max() <= L * sfa_batch
-                    loc = so - l * sfa_batch
-                    assert valid_sfa[loc].all() and valid_sfa[loc + 1].all(), "scale read hits padding"
-                    slots = np.concatenate([lds_slot(ci - c0, q) for q in range(4)])
-                    assert slots.max() < lds_slots
-        for i in range(K_ROWS):
-            r = tile * rows_wg + (wave * G + grp) * K_ROWS + i
-            # one writer lane (j == 0) per row group and row; for split shapes
-            # count each row once (the finishing WG writes the whole tile)
-            w_rows = r[(j == 0) & (r < M)]
-            if S == 1 or s == S - 1:
-                np.add.at(written, l * M + w_rows, 1)
+        row_base = (slot0 >> 5) << 7
+        a_begin = (l * M + row_base) * (K // 2)
+        num_records = min(a_bytes - a_begin, 2 ** 31 - 1)
+        nsteps = cdiv(nq, G) * CPL
+        rows_all = slot_row(slot0, np.arange(nq))
+        for c0 in range(c_begin, c_end, SEG):
+            nck = min(SEG, c_end - c0)
+            # ---- A: every step, including the prefetch issued past the end
+            last = cdiv(nsteps, PREFETCH) * PREFETCH + PREFETCH
+            for t in range(last):
+                q = np.minimum(grp + G * (t // CPL), nq - 1)
+                r = np.minimum(slot_row(slot0, q), M - 1)
+                ci = c0 + np.minimum(j + (t % CPL) * lpr, nck - 1)
+                off = (r - row_base) * (K // 2) + ci * 16
+                assert off.min() >= 0 and (off + 16).max() <= num_records, "A read outside the resource"
+            # ---- staging: LDS byte -> global scale byte
+            dst_all, src_all = [], []
+            if layout == 1:
+                ncb_seg, cb0 = (nck + 1) >> 1, c0 >> 1
+                items = nslots * ncb_seg
+                assert items <= STAGE_MAX * THREADS, "staging items not covered"
+                it = np.arange(items)
+                sl, cb = it % nslots, it // nslots
+                sg = slot0 + sl
+                src = l * sfa_batch + ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
+                assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
+                for i4 in range(4):
+                    dst = (sl * 4 + i4) * segb + cb * 4
+                    assert (dst + 4).max() <= nq * segb
+                    for b in range(4):
+                        dst_all.append(dst + b)
+                        src_all.append(src + 4 * i4 + b)
+            elif wide_plain:
+                units = nck >> 3
+                assert nck % 8 == 0
+                items = nq * units
+                assert items <= STAGE_MAX * THREADS, "staging items not covered"
+                it = np.arange(items)
+                q, u = it // units, it % units
+                r = np.minimum(slot_row(slot0, q), M - 1)
+                src = l * sfa_batch + r * nkb + 2 * c0 + 16 * u
+                assert (2 * c0 + 16 * u + 16).max() <= nkb
+                assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
+                dst = q * segb + 16 * u
+                assert (dst + 16).max() <= nq * segb
+                for b in range(16):
+                    dst_all.append(dst + b)
+                    src_all.append(src + b)
+            else:
+                it = np.arange(nq * nck)
+                q, c = it // nck, it % nck
+                r = np.minimum(slot_row(slot0, q), M - 1)
+                src = l * sfa_batch + r * nkb + 2 * (c0 + c)
+                assert src.min() >= 0 and (src + 2).max() <= L * sfa_batch
+                dst = q * segb + 2 * c
+                assert (dst + 2).max() <= nq * segb
+                for b in range(2):
+                    dst_all.append(dst + b)
+                    src_all.append(src + b)
+            lds_src = np.full(nq * segb, -1, np.int64)
+            lds_src[np.concatenate(dst_all)] = np.concatenate(src_all)
+            # ---- b': B chunk and its two SFB scales
+            for k in range(CPL):
+                ci = c0 + np.minimum(j + k * lpr, nck - 1)
+                boff = l * (K // 2) + ci * 16
+                assert boff.min() >= 0 and (boff + 16).max() <= b_size
+                so = sf_offset(layout, np.zeros_like(ci), 2 * ci, nkb, ncb)
+                assert (so + 1).max() < sfb_batch
+                assert valid_sfb[so].all() and valid_sfb[so + 1].all()
+            # ---- compute side: every real (row, chunk) reads the LDS bytes
+            # that were staged from that row's two scales of that chunk
+            qs = np.arange(nq)[rows_all < M]
+            if qs.size:
+                qq, cl, b = np.meshgrid(qs, np.arange(nck), np.arange(2), indexing="ij")
+                rq = rows_all[qq]
+                want = l * sfa_batch + sf_offset(layout, rq, 2 * (c0 + cl) + b, nkb, ncb)
+                got = lds_src[qq * segb + 2 * cl + b]
+                assert np.array_equal(got, want), "staged scales do not match what the compute reads"
+                assert valid_sfa[want - l * sfa_batch].all()
+        # ---- outputs
+        real = rows_all[rows_all < M]
+        if S == 1 or s == S - 1:
+            np.add.at(written, l * M + real, 1)
         if S > 1:
-            assert n_tiles * L < 1024, "more tickets than the fixed ticket region holds"
+            assert P * L <= 1024, "more tickets than the ticket region holds"
             ws_part = cdiv(L * M * S * 4, 256) * 256
-            assert g.nvfp4_gemv_workspace_bytes(M, K, L) == 4096 + ws_part
-            rows = tile * rows_wg + np.arange(rows_wg)
-            rows = rows[rows < M]
-            assert ((l * M + rows) * S + s).max() < L * M * S
-            assert l * n_tiles + tile < n_tiles * L
+            assert ws_bytes == 4096 + ws_part
+            assert ((l * M + real) * S + s).max() < L * M * S
+            assert l * P + tile < P * L
     assert np.all(written == 1), "some output row is written zero or several times"
 
 
@@ -142,7 +189,7 @@ SHAPES = sorted({(w.M, w.K, w.L) for w in synth.ALL} |
                  (3, 4096, 7), (16, 32, 1), (256, 32, 1), (2, 32, 256), (128, 128, 1),
                  (127, 16384, 3), (1000, 16384, 3), (7168, 2048, 4), (5, 32768, 2),
                  (33, 8192, 1), (1000, 4096, 3), (1000, 4096, 1), (256, 2048, 2), (4, 128, 16),
-                 (7168, 32768, 1), (64, 65536, 1), (300, 20480, 2)})
+                 (7168, 32768, 1), (64, 65536, 1), (300, 20480, 2), (16, 256, 256), (2, 16384, 16)})
 
 
 @pytest.mark.parametrize("M,K,L", SHAPES)

@@ -52,6 +52,7 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
@@ -68,6 +69,7 @@ constexpr int kCachePolicyNT = 2;         // buffer load cache policy: non-tempo
 constexpr int64_t kMaxK = INT64_C(1) << 22; // keeps one workgroup's A offsets below 2^31
 
 static_assert(kPrefetch % kCpl == 0, "a row's chunk-steps must not straddle the prefetch ring");
+static_assert(kCpl == 4, "one 8-byte LDS read carries a lane's scales of one row");
 static_assert(kStageMax * kThreads * 16 >= kSfaLdsBudget, "staging registers cover the LDS budget");
 
 struct Params {
@@ -100,6 +102,13 @@ __device__ inline int32_t slot_row(int32_t slot0, int32_t q)
 {
     const int32_t s = slot0 + (q >> 2);
     return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31);
+}
+
+// Pair slot of segment chunk c in a staged scale row: lane c % LPR, step c / LPR.
+template <int LPR>
+__device__ inline int32_t pair_slot(int32_t c)
+{
+    return (c % LPR) * kCpl + c / LPR;
 }
 
 // Byte offset of the two scales of chunk c (blocks 2c, 2c+1) of row r.
@@ -252,7 +261,6 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
         kBufferFlags);
 
     const int32_t NR = (nq + G - 1) / G;                   // row rounds per group
-    const int32_t nsteps = NR * kCpl;                      // one step = one chunk of one row
 
     for (int32_t c0 = c_begin; c0 < c_end; c0 += SEG) {
         const int32_t nck = min(SEG, c_end - c0);
@@ -263,12 +271,22 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
         // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
         // the end read a clamped (valid) chunk so that every load is
         // unconditional and the wait counts stay exact.
-        auto a_off = [&](int32_t t) -> uint32_t {
-            const int32_t q = min(grp + G * (t / kCpl), nq - 1);
+        // Byte offsets into A: round n of the group reads row slot_row(q_n)
+        // (clamped to a real row); step k of a round reads the lane's chunk k
+        // (clamped to a real chunk; its contribution is masked by live[k]).
+        auto row_off = [&](int32_t n) -> uint32_t {
+            const int32_t q = min(grp + G * n, nq - 1);
             const int32_t r = min(slot_row(slot0, q), M - 1);
-            const int32_t ci = c0 + min(j + (t % kCpl) * LPR, nck - 1);
-            return (uint32_t)(r - row_base) * (uint32_t)(K >> 1) + (uint32_t)ci * 16u;
+            return (uint32_t)(r - row_base) * (uint32_t)(K >> 1);
         };
+        uint32_t choff[kCpl];
+        bool live[kCpl];
+#pragma unroll
+        for (int k = 0; k < kCpl; ++k) {
+            const int32_t cl = j + k * LPR;
+            live[k] = cl < nck;
+            choff[k] = (uint32_t)(c0 + min(cl, nck - 1)) * 16u;
+        }
         uint4_t abuf[kPrefetch];
         uint4_t bload[kCpl];
         uint32_t sload[kCpl];
@@ -282,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kPrefetch; ++u)
-                abuf[u] = load_a(arsrc, a_off(u));
+                abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -290,7 +308,10 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
         // first kPrefetch steps of A. Vector loads complete in order, so the
         // staging and the b' decode wait only for their own loads while A is
         // still in flight.
-        // ---- scales of this workgroup's rows and segment -> LDS, layout [q][block]
+        // ---- scales of this workgroup's rows and segment -> LDS. Layout: row q
+        // holds, for each lane j of a row group, the 2*kCpl scale bytes of its
+        // chunks j, j+LPR, ... (chunk c at pair slot (c % LPR) * kCpl + c / LPR),
+        // so one 8-byte read gives a lane all the scales of a row.
         if (LAYOUT == NVFP4_SF_BLOCKED) {
             // item (slot, 4-block group): one 16-byte vector = 4 rows x 4 blocks
             const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1;
@@ -308,11 +329,14 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
             for (int i = 0; i < kStageMax; ++i) {
                 const int32_t it = min(tid + i * kThreads, items - 1);
                 const int32_t sl = it % nslots, cb = it / nslots;
-                uint8_t *dst = lds + (size_t)(sl * 4) * segb + cb * 4;
-                *(uint32_t *)(dst) = v[i].x;
-                *(uint32_t *)(dst + segb) = v[i].y;
-                *(uint32_t *)(dst + 2 * segb) = v[i].z;
-                *(uint32_t *)(dst + 3 * segb) = v[i].w;
+                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};   // rows i4 = 0..3
+                uint8_t *row0 = lds + (size_t)(sl * 4) * segb;
+                const int32_t p0 = pair_slot<LPR>(2 * cb), p1 = pair_slot<LPR>(2 * cb + 1);
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    *(uint16_t *)(row0 + i4 * segb + 2 * p0) = (uint16_t)w4[i4];
+                    *(uint16_t *)(row0 + i4 * segb + 2 * p1) = (uint16_t)(w4[i4] >> 16);
+                }
             }
         } else if (p.wide_plain) {
             // item (row, 8 chunks): 16 contiguous bytes of a plain scale row
@@ -331,7 +355,11 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
             for (int i = 0; i < kStageMax; ++i) {
                 const int32_t it = min(tid + i * kThreads, items - 1);
                 const int32_t q = it / units, u = it % units;
-                *(uint4_t *)(lds + (size_t)q * segb + 16 * u) = v[i];
+                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};   // chunks 8u .. 8u+7
+                uint8_t *row = lds + (size_t)q * segb;
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    *(uint16_t *)(row + 2 * pair_slot<LPR>(8 * u + h)) = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
             }
         } else {
             // item (row, chunk): the two scales of one chunk
@@ -339,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
             for (int32_t it = tid; it < nq * nck; it += kThreads) {
                 const int32_t q = it / nck, c = it % nck;
                 const int32_t r = min(slot_row(slot0, q), M - 1);
-                *(uint16_t *)(lds + (size_t)q * segb + 2 * c) =
+                *(uint16_t *)(lds + (size_t)q * segb + 2 * pair_slot<LPR>(c)) =
                     *(const uint16_t *)(sfa_l + (int64_t)r * nkb + 2 * (c0 + c));
             }
         }
@@ -351,34 +379,46 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
             make_bprime(bload[k], sload[k], bp[k]);
         __syncthreads();
 
-        // ---- the group's rows one after another, kPrefetch chunk loads ahead
-        float acc = 0.0f;
-        for (int32_t t0 = 0; t0 < nsteps; t0 += kPrefetch) {
+        // ---- the group's rows one after another, kPrefetch chunk loads ahead.
+        // A round is one row: kCpl steps, one 16-byte chunk each. The scales of
+        // the next round are read from LDS one round early.
+        constexpr int PR = kPrefetch / kCpl;               // rounds in the load ring
+        auto sfa_of = [&](int32_t n) -> uint2_t {
+            const int32_t q = min(grp + G * n, nq - 1);
+            return *(const uint2_t *)(lds + (size_t)q * segb + j * (2 * kCpl));
+        };
+        uint2_t sf_next = sfa_of(0);
+        for (int32_t n0 = 0; n0 < NR; n0 += PR) {
 #pragma unroll
-            for (int u = 0; u < kPrefetch; ++u) {
-                const int k = u % kCpl;                    // t0 % kCpl == 0
-                const int32_t t = t0 + u;
-                const int32_t q = grp + G * (t / kCpl);
-                const int32_t qc = min(q, nq - 1);
-                const int32_t cl = j + k * LPR;            // chunk inside the segment
-                const uint32_t sv = *(const uint16_t *)(lds + (size_t)qc * segb + 2 * min(cl, nck - 1));
-                const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sv, false);
-                const uint4_t a = abuf[u];
-                const float lo = dot_block(a.x, a.y, bp[k][0], bp[k][1]);
-                const float hi = dot_block(a.z, a.w, bp[k][2], bp[k][3]);
-                const float base = k == 0 ? 0.0f : acc;
-                const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, base));
-                acc = cl < nck ? nacc : base;
-                // refill the slot only after its last use: a load hoisted above
-                // the use would need a second register set and copies that wait
-                __builtin_amdgcn_sched_barrier(0);
-                abuf[u] = load_a(arsrc, a_off(t + kPrefetch));
-                if (k == kCpl - 1) {
-                    const float v = group_sum<RED>(acc);
-                    if (leader && q < nq) {
-                        float *dst = part + q * WPG + wig;
-                        *dst = first ? v : *dst + v;
-                    }
+            for (int rr = 0; rr < PR; ++rr) {
+                const int32_t n = n0 + rr;
+                const int32_t q = grp + G * n;
+                const uint2_t sfc = sf_next;
+                sf_next = sfa_of(n + 1);
+                const uint32_t ro_refill = row_off(n + PR);
+                const float2_t sfk[kCpl] = {__builtin_amdgcn_cvt_pk_f32_fp8(sfc.x, false),
+                                            __builtin_amdgcn_cvt_pk_f32_fp8(sfc.x, true),
+                                            __builtin_amdgcn_cvt_pk_f32_fp8(sfc.y, false),
+                                            __builtin_amdgcn_cvt_pk_f32_fp8(sfc.y, true)};
+                float acc = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kCpl; ++k) {
+                    const int u = rr * kCpl + k;
+                    const float2_t sf = sfk[k];
+                    const uint4_t a = abuf[u];
+                    const float lo = dot_block(a.x, a.y, bp[k][0], bp[k][1]);
+                    const float hi = dot_block(a.z, a.w, bp[k][2], bp[k][3]);
+                    const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc));
+                    acc = live[k] ? nacc : acc;
+                    // refill the slot only after its last use: a load hoisted above
+                    // the use would need a second register set and copies that wait
+                    __builtin_amdgcn_sched_barrier(0);
+                    abuf[u] = load_a(arsrc, ro_refill + choff[k]);
+                }
+                const float v = group_sum<RED>(acc);
+                if (leader && q < nq) {
+                    float *dst = part + q * WPG + wig;
+                    *dst = first ? v : *dst + v;
                 }
             }
         }
@@ -488,12 +528,12 @@ int choose_lpr(int64_t nc)
     return std::min<int>(kMaxLpr, pow2_ceil(cdiv(nc, kCpl)));
 }
 
-// LDS bytes per staged scale row: 2 bytes per chunk of the segment, padded so
-// that the rows read together by the groups of one wave start on other banks.
+// LDS bytes per staged scale row: 2 bytes per chunk of the segment. The groups
+// of one wave read consecutive rows, 2*kCpl bytes per lane, i.e. one
+// contiguous run of LDS.
 int seg_bytes(int lpr)
 {
-    const int raw = 2 * kCpl * lpr + (lpr < 64 ? 2 * lpr : 0);
-    return (int)align_up((size_t)raw, 16);
+    return (int)align_up((size_t)(2 * kCpl * lpr), 16);
 }
 
 nvfp4_status_t check_shape(int64_t M, int64_t K, int64_t L)

@@ -20,7 +20,7 @@ import pytest
 import block_scaled_fp4_gemv_amd as g
 import synth
 
-THREADS, CPL, PREFETCH, STAGE_MAX, XCDS = 256, 4, 8, 12, 8
+THREADS, CPL, PREFETCH, STAGE_MAX, XCDS, MAX_TICKETS = 256, 4, 8, 12, 8, 1024
 
 
 def cdiv(a, b):
@@ -38,9 +38,13 @@ def slot_row(slot0, q):
     return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31)
 
 
-def seg_bytes(lpr):
-    raw = 2 * CPL * lpr + (2 * lpr if lpr < 64 else 0)
-    return cdiv(raw, 16) * 16
+def seg_bytes(lpr, cpl=CPL):
+    return cdiv(2 * cpl * lpr, 16) * 16
+
+
+def pair_slot(c, lpr, cpl=CPL):
+    """Pair slot of segment chunk c in a staged scale row (lane c % lpr, step c / lpr)."""
+    return (c % lpr) * cpl + c // lpr
 
 
 def sf_offset(layout, r, kb, nkb, ncb):
@@ -50,7 +54,11 @@ def sf_offset(layout, r, kb, nkb, ncb):
     return ((r >> 7) * ncb + (kb >> 2)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (kb & 3)
 
 
-def check_shape(M, K, L, layout, plan=None, workspace_bytes=None):
+def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREADS, cpl=CPL,
+                prefetch=PREFETCH, stage_max=STAGE_MAX, max_tickets=MAX_TICKETS):
+    """Walk the whole grid of one launch. ``plan``/``workspace_bytes`` default
+    to the built library's; the constants can be overridden to check a variant."""
+    THREADS, CPL, PREFETCH, STAGE_MAX = threads, cpl, prefetch, stage_max
     p = (plan or g.nvfp4_gemv_plan)(M, K, L)
     ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
     lpr, spw, S = p["lanes_per_row"], p["rows_per_wg"] // 4, p["k_splits"]
@@ -62,7 +70,7 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None):
     P = cdiv(ns, spw)
     assert n_wg == P * L * S
     SEG, G, WPG = lpr * CPL, THREADS // lpr, max(1, lpr // 64)
-    segb = seg_bytes(lpr)
+    segb = seg_bytes(lpr, CPL)
     assert lds_bytes == 4 * spw * segb + 4 * spw * WPG * 4
     assert lds_bytes <= 64 * 1024
     wide_plain = nchunks % 8 == 0 and kc % 8 == 0
@@ -117,12 +125,13 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None):
                 sg = slot0 + sl
                 src = l * sfa_batch + ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
                 assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
+                p0, p1 = pair_slot(2 * cb, lpr, CPL), pair_slot(2 * cb + 1, lpr, CPL)
                 for i4 in range(4):
-                    dst = (sl * 4 + i4) * segb + cb * 4
-                    assert (dst + 4).max() <= nq * segb
-                    for b in range(4):
-                        dst_all.append(dst + b)
-                        src_all.append(src + 4 * i4 + b)
+                    row = (sl * 4 + i4) * segb
+                    assert (row + 2 * np.maximum(p0, p1) + 2).max() <= nq * segb
+                    for b in range(2):
+                        dst_all += [row + 2 * p0 + b, row + 2 * p1 + b]
+                        src_all += [src + 4 * i4 + b, src + 4 * i4 + 2 + b]
             elif wide_plain:
                 units = nck >> 3
                 assert nck % 8 == 0
@@ -134,18 +143,19 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None):
                 src = l * sfa_batch + r * nkb + 2 * c0 + 16 * u
                 assert (2 * c0 + 16 * u + 16).max() <= nkb
                 assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
-                dst = q * segb + 16 * u
-                assert (dst + 16).max() <= nq * segb
-                for b in range(16):
-                    dst_all.append(dst + b)
-                    src_all.append(src + b)
+                for h in range(8):
+                    dst = q * segb + 2 * pair_slot(8 * u + h, lpr, CPL)
+                    assert (dst + 2).max() <= nq * segb
+                    for b in range(2):
+                        dst_all.append(dst + b)
+                        src_all.append(src + 2 * h + b)
             else:
                 it = np.arange(nq * nck)
                 q, c = it // nck, it % nck
                 r = np.minimum(slot_row(slot0, q), M - 1)
                 src = l * sfa_batch + r * nkb + 2 * (c0 + c)
                 assert src.min() >= 0 and (src + 2).max() <= L * sfa_batch
-                dst = q * segb + 2 * c
+                dst = q * segb + 2 * pair_slot(c, lpr, CPL)
                 assert (dst + 2).max() <= nq * segb
                 for b in range(2):
                     dst_all.append(dst + b)
@@ -160,14 +170,17 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None):
                 so = sf_offset(layout, np.zeros_like(ci), 2 * ci, nkb, ncb)
                 assert (so + 1).max() < sfb_batch
                 assert valid_sfb[so].all() and valid_sfb[so + 1].all()
-            # ---- compute side: every real (row, chunk) reads the LDS bytes
-            # that were staged from that row's two scales of that chunk
+            # ---- compute side: lane j reads 2*CPL bytes at q*segb + j*2*CPL (any
+            # q < nq); every real (row, chunk) finds there the bytes staged from
+            # that row's two scales of that chunk
+            assert (np.arange(lpr) * 2 * CPL + 2 * CPL).max() <= segb
             qs = np.arange(nq)[rows_all < M]
             if qs.size:
                 qq, cl, b = np.meshgrid(qs, np.arange(nck), np.arange(2), indexing="ij")
                 rq = rows_all[qq]
                 want = l * sfa_batch + sf_offset(layout, rq, 2 * (c0 + cl) + b, nkb, ncb)
-                got = lds_src[qq * segb + 2 * cl + b]
+                jj, kk = cl % lpr, cl // lpr
+                got = lds_src[qq * segb + (jj * CPL + kk) * 2 + b]
                 assert np.array_equal(got, want), "staged scales do not match what the compute reads"
                 assert valid_sfa[want - l * sfa_batch].all()
         # ---- outputs
@@ -175,9 +188,9 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None):
         if S == 1 or s == S - 1:
             np.add.at(written, l * M + real, 1)
         if S > 1:
-            assert P * L <= 1024, "more tickets than the ticket region holds"
+            assert P * L <= max_tickets, "more tickets than the ticket region holds"
             ws_part = cdiv(L * M * S * 4, 256) * 256
-            assert ws_bytes == 4096 + ws_part
+            assert ws_bytes == 4 * max_tickets + ws_part
             assert ((l * M + real) * S + s).max() < L * M * S
             assert l * P + tile < P * L
     assert np.all(written == 1), "some output row is written zero or several times"

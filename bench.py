@@ -13,9 +13,12 @@ Timing:
   * timed region: exactly K steps captured in one HIP graph (so host launch
     overhead is not measured), replayed once between two synchronisations;
     GPU time from events around the replay gives ms_per_step and ``value``.
-  * per-kernel duration for the roofline: the same K calls launched eagerly,
-    each between two events on the launch stream, behind a spin kernel that
-    lets the host queue them all first.
+  * the roofline's ``achieved`` divides the ideal bytes by the average launch
+    duration over the timed region (GPU time of the replay / K: one kernel per
+    step, so this includes the short gaps between back-to-back kernels).
+  * ``kernel_us`` (extra): the same K calls launched eagerly, each between two
+    events on the launch stream, behind a spin kernel that lets the host queue
+    them all first.
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -224,7 +227,7 @@ def main():
 
     ideal = w.ideal_bytes
     value_gbs = ideal / (ms_per_step * 1e-3) / 1e9
-    achieved = ideal / (kern_avg * 1e-6) / 1e9
+    achieved = ideal / (ms_per_step * 1e-3) / 1e9     # average launch over the timed region
     traffic = traffic_from_profile(w.name, layout)
     out = {
         "metric": METRIC,

@@ -43,6 +43,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "nvfp4_gemv.h"
@@ -77,7 +78,7 @@ struct Params {
     int32_t S;            // K-slices
     int32_t kc_split;     // chunks per K-slice
     int32_t P;            // workgroups per (batch, slice)
-    int32_t spw;          // slots per workgroup
+    int32_t spw;          // slots per workgroup (at most)
     int32_t ns;           // slots per batch that hold at least one row
     int32_t segb;         // LDS bytes per row of staged scales
     int32_t wide_plain;   // plain scales staged in 16-byte units
@@ -96,11 +97,11 @@ __device__ inline uint32_t xcd_remap(uint32_t i, uint32_t n)
     return x * q + min(x, r) + j;
 }
 
-// Row of local row q of a workgroup whose first slot is slot0: slot
-// slot0 + q/4, sub-row q%4 (the 32-row group inside the 128-row block).
-__device__ inline int32_t slot_row(int32_t slot0, int32_t q)
+// Row of local row q of a workgroup whose first slot is first: slot
+// first + q/4, sub-row q%4 (the 32-row group inside the 128-row block).
+__device__ inline int32_t slot_row(int32_t first, int32_t q)
 {
-    const int32_t s = slot0 + (q >> 2);
+    const int32_t s = first + (q >> 2);
     return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31);
 }
 
@@ -233,8 +234,10 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
 
     const int32_t M = p.M, K = p.K, segb = p.segb;
     const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
-    const int32_t slot0 = tile * p.spw;
-    const int32_t nslots = min(p.spw, p.ns - slot0);
+    // Slots of this workgroup: a contiguous range, so that its blocked scales
+    // are few whole lines per 512-byte tile (neighbouring slots share a line).
+    const int32_t first = tile * p.spw;
+    const int32_t nslots = min(p.spw, p.ns - first);
     const int32_t nq = 4 * nslots;                        // local rows (some may be >= M)
     const int32_t c_begin = s * p.kc_split;
     const int32_t c_end = min(c_begin + p.kc_split, nchunks);
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     // A through a buffer resource based at the first row of this workgroup's
     // first 128-row block: 32-bit lane offsets (the rows of one workgroup lie
     // within a few blocks), and lanes past the end of A read zero.
-    const int32_t row_base = (slot0 >> 5) << 7;
+    const int32_t row_base = (first >> 5) << 7;
     const int64_t a_begin = (abatch + row_base) * (int64_t)(K >> 1);
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(A + a_begin), (short)0, (int)min(p.a_bytes - a_begin, (int64_t)0x7FFFFFFF),
@@ -262,10 +265,25 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
 
     const int32_t NR = (nq + G - 1) / G;                   // row rounds per group
 
+    // The scales of the workgroup's rows and K-segment are staged into LDS with
+    // 16-byte loads issued after the first kPrefetch A loads, so that the first
+    // rows never wait for them: the first PR row rounds (the ones already in
+    // the load ring) keep their exact 16-element block sums in registers and
+    // apply the scales once the staged scales are published behind a barrier.
+    // The staging loads go through a buffer resource: a fixed number per thread
+    // keeps the wait counts of the A stream exact, and the unused ones get an
+    // out-of-range offset, which returns zero without a memory access.
+    constexpr int PR = kPrefetch / kCpl;               // rounds in the load ring
+    const int64_t sfa_base = LAYOUT == NVFP4_SF_BLOCKED ? (int64_t)(first >> 5) * ncb * 512
+                                                        : (int64_t)row_base * nkb;
+    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(sfa_l + sfa_base), (short)0,
+        (int)min(p.sfa_batch - sfa_base, (int64_t)0x7FFFFFFF), kBufferFlags);
+
     for (int32_t c0 = c_begin; c0 < c_end; c0 += SEG) {
         const int32_t nck = min(SEG, c_end - c0);
-        const bool first = c0 == c_begin;
-        if (!first)
+        const bool first_seg = c0 == c_begin;
+        if (!first_seg)
             __syncthreads();                               // previous segment's LDS reads done
 
         // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
@@ -276,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
         // (clamped to a real chunk; its contribution is masked by live[k]).
         auto row_off = [&](int32_t n) -> uint32_t {
             const int32_t q = min(grp + G * n, nq - 1);
-            const int32_t r = min(slot_row(slot0, q), M - 1);
+            const int32_t r = min(slot_row(first, q), M - 1);
             return (uint32_t)(r - row_base) * (uint32_t)(K >> 1);
         };
         uint32_t choff[kCpl];
@@ -287,86 +305,93 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
             live[k] = cl < nck;
             choff[k] = (uint32_t)(c0 + min(cl, nck - 1)) * 16u;
         }
+
+        // ---- staging items. Blocked: item (slot, 4-block group) is one 16-byte
+        // vector = 4 rows x 4 blocks. Wide plain: item (row, 8 chunks) is 16
+        // contiguous bytes of a plain scale row. LDS layout: row q holds, for
+        // each lane j of a row group, the 2*kCpl scale bytes of its chunks j,
+        // j+LPR, ... (chunk c at pair slot (c % LPR) * kCpl + c / LPR), so one
+        // 8-byte read gives a lane all the scales of a row.
+        const bool direct = LAYOUT == NVFP4_SF_PLAIN && !p.wide_plain;
+        const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1, units = nck >> 3;
+        const int32_t items = LAYOUT == NVFP4_SF_BLOCKED ? nslots * ncb_seg : (direct ? 0 : nq * units);
+        uint4_t sv[kStageMax];
+        auto stage_load = [&]() {
+#pragma unroll
+            for (int i = 0; i < kStageMax; ++i) {
+                const int32_t it = tid + i * kThreads;
+                uint32_t off = 0x80000000u;
+                if (LAYOUT == NVFP4_SF_BLOCKED) {
+                    const int32_t sg = first + it % nslots, cb = it / nslots;
+                    if (it < items)
+                        off = (uint32_t)((((sg >> 5) - (first >> 5)) * ncb + cb0 + cb) * 512 + (sg & 31) * 16);
+                } else {
+                    const int32_t q = it / max(units, 1), u = it % max(units, 1);
+                    const int32_t r = min(slot_row(first, min(q, nq - 1)), M - 1);
+                    if (it < items)
+                        off = (uint32_t)((r - row_base) * nkb + 2 * c0 + 16 * u);
+                }
+                sv[i] = __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)off, 0, 0);
+            }
+            // keep every load here: a load sunk into the conditional writes
+            // below would be waited for together with the whole load ring
+            asm volatile("" ::: "memory");
+        };
+        auto stage_write = [&]() {
+            // recompute the item indices here instead of keeping those of the
+            // loads alive across the first rounds
+            int32_t t = tid;
+            asm volatile("" : "+v"(t));
+#pragma unroll
+            for (int i = 0; i < kStageMax; ++i) {
+                const int32_t it = t + i * kThreads;
+                if (it >= items)
+                    break;
+                const uint32_t w4[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
+                if (LAYOUT == NVFP4_SF_BLOCKED) {
+                    const int32_t sl = it % nslots, cb = it / nslots;
+                    uint8_t *row0 = lds + (size_t)(sl * 4) * segb;     // rows i4 = 0..3
+                    const int32_t p0 = pair_slot<LPR>(2 * cb), p1 = pair_slot<LPR>(2 * cb + 1);
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        *(uint16_t *)(row0 + i4 * segb + 2 * p0) = (uint16_t)w4[i4];
+                        *(uint16_t *)(row0 + i4 * segb + 2 * p1) = (uint16_t)(w4[i4] >> 16);
+                    }
+                } else {
+                    const int32_t q = it / units, u = it % units;
+                    uint8_t *row = lds + (size_t)q * segb;         // chunks 8u .. 8u+7
+#pragma unroll
+                    for (int h = 0; h < 8; ++h)
+                        *(uint16_t *)(row + 2 * pair_slot<LPR>(8 * u + h)) = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
+                }
+            }
+        };
+
+        // Loads are issued in this order: B and SFB for b', the first kPrefetch
+        // steps of A, the staged scales. Vector loads complete in order, so
+        // each consumer waits only for its own loads and the ones before them.
         uint4_t abuf[kPrefetch];
         uint4_t bload[kCpl];
         uint32_t sload[kCpl];
-        auto load_bprime_and_a = [&]() {
 #pragma unroll
-            for (int k = 0; k < kCpl; ++k) {
-                const int32_t ci = c0 + min(j + k * LPR, nck - 1);
-                bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
-                sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < kCpl; ++k) {
+            const int32_t ci = c0 + min(j + k * LPR, nck - 1);
+            bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
+            sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kPrefetch; ++u)
-                abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
-            __builtin_amdgcn_sched_barrier(0);
-        };
+        for (int u = 0; u < kPrefetch; ++u)
+            abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load();
+        __builtin_amdgcn_sched_barrier(0);
 
-        // Loads are issued in this order: scales to stage, B for b', then the
-        // first kPrefetch steps of A. Vector loads complete in order, so the
-        // staging and the b' decode wait only for their own loads while A is
-        // still in flight.
-        // ---- scales of this workgroup's rows and segment -> LDS. Layout: row q
-        // holds, for each lane j of a row group, the 2*kCpl scale bytes of its
-        // chunks j, j+LPR, ... (chunk c at pair slot (c % LPR) * kCpl + c / LPR),
-        // so one 8-byte read gives a lane all the scales of a row.
-        if (LAYOUT == NVFP4_SF_BLOCKED) {
-            // item (slot, 4-block group): one 16-byte vector = 4 rows x 4 blocks
-            const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1;
-            const int32_t items = nslots * ncb_seg;
-            uint4_t v[kStageMax];
-#pragma unroll
-            for (int i = 0; i < kStageMax; ++i) {
-                const int32_t it = min(tid + i * kThreads, items - 1);
-                const int32_t sl = it % nslots, cb = it / nslots, sg = slot0 + sl;
-                v[i] = *(const uint4_t *)(sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16);
-            }
-            load_bprime_and_a();
-            // items past the end repeat the last item: same bytes, same place
-#pragma unroll
-            for (int i = 0; i < kStageMax; ++i) {
-                const int32_t it = min(tid + i * kThreads, items - 1);
-                const int32_t sl = it % nslots, cb = it / nslots;
-                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};   // rows i4 = 0..3
-                uint8_t *row0 = lds + (size_t)(sl * 4) * segb;
-                const int32_t p0 = pair_slot<LPR>(2 * cb), p1 = pair_slot<LPR>(2 * cb + 1);
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    *(uint16_t *)(row0 + i4 * segb + 2 * p0) = (uint16_t)w4[i4];
-                    *(uint16_t *)(row0 + i4 * segb + 2 * p1) = (uint16_t)(w4[i4] >> 16);
-                }
-            }
-        } else if (p.wide_plain) {
-            // item (row, 8 chunks): 16 contiguous bytes of a plain scale row
-            const int32_t units = nck >> 3;                // nck % 8 == 0 on this path
-            const int32_t items = nq * units;
-            uint4_t v[kStageMax];
-#pragma unroll
-            for (int i = 0; i < kStageMax; ++i) {
-                const int32_t it = min(tid + i * kThreads, items - 1);
-                const int32_t q = it / units, u = it % units;
-                const int32_t r = min(slot_row(slot0, q), M - 1);
-                v[i] = *(const uint4_t *)(sfa_l + (int64_t)r * nkb + 2 * c0 + 16 * u);
-            }
-            load_bprime_and_a();
-#pragma unroll
-            for (int i = 0; i < kStageMax; ++i) {
-                const int32_t it = min(tid + i * kThreads, items - 1);
-                const int32_t q = it / units, u = it % units;
-                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};   // chunks 8u .. 8u+7
-                uint8_t *row = lds + (size_t)q * segb;
-#pragma unroll
-                for (int h = 0; h < 8; ++h)
-                    *(uint16_t *)(row + 2 * pair_slot<LPR>(8 * u + h)) = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
-            }
-        } else {
-            // item (row, chunk): the two scales of one chunk
-            load_bprime_and_a();
+        if (direct) {
+            // item (row, chunk): the two scales of one chunk, copied directly
             for (int32_t it = tid; it < nq * nck; it += kThreads) {
                 const int32_t q = it / nck, c = it % nck;
-                const int32_t r = min(slot_row(slot0, q), M - 1);
+                const int32_t r = min(slot_row(first, q), M - 1);
                 *(uint16_t *)(lds + (size_t)q * segb + 2 * pair_slot<LPR>(c)) =
                     *(const uint16_t *)(sfa_l + (int64_t)r * nkb + 2 * (c0 + c));
             }
@@ -377,50 +402,95 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
 #pragma unroll
         for (int k = 0; k < kCpl; ++k)
             make_bprime(bload[k], sload[k], bp[k]);
-        __syncthreads();
 
         // ---- the group's rows one after another, kPrefetch chunk loads ahead.
         // A round is one row: kCpl steps, one 16-byte chunk each. The scales of
         // the next round are read from LDS one round early.
-        constexpr int PR = kPrefetch / kCpl;               // rounds in the load ring
         auto sfa_of = [&](int32_t n) -> uint2_t {
             const int32_t q = min(grp + G * n, nq - 1);
             return *(const uint2_t *)(lds + (size_t)q * segb + j * (2 * kCpl));
         };
-        uint2_t sf_next = sfa_of(0);
-        for (int32_t n0 = 0; n0 < NR; n0 += PR) {
-#pragma unroll
-            for (int rr = 0; rr < PR; ++rr) {
-                const int32_t n = n0 + rr;
-                const int32_t q = grp + G * n;
+        auto decode_sfa = [&](uint2_t w, float2_t (&sfk)[kCpl]) {
+            sfk[0] = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false);
+            sfk[1] = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+            sfk[2] = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false);
+            sfk[3] = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+        };
+        auto store_row = [&](int32_t q, float acc) {
+            const float v = group_sum<RED>(acc);
+            if (leader && q < nq) {
+                float *dst = part + q * WPG + wig;
+                *dst = first_seg ? v : *dst + v;
+            }
+        };
+        // One round: block sums of the lane's chunks against b', then (SCALED)
+        // the scales, the row sum and its store; the ring slot is refilled with
+        // the step PR rounds ahead.
+        float2_t bsum[PR][kCpl];                         // block sums of the first rounds
+        uint2_t sf_next = {0u, 0u};
+        auto round = [&](auto scaled, int32_t n, int rr) {
+            constexpr bool SCALED = decltype(scaled)::value;
+            const uint32_t ro_refill = row_off(n + PR);
+            float2_t sfk[kCpl];
+            if (SCALED) {
                 const uint2_t sfc = sf_next;
                 sf_next = sfa_of(n + 1);
-                const uint32_t ro_refill = row_off(n + PR);
-                const float2_t sfk[kCpl] = {__builtin_amdgcn_cvt_pk_f32_fp8(sfc.x, false),
-                                            __builtin_amdgcn_cvt_pk_f32_fp8(sfc.x, true),
-                                            __builtin_amdgcn_cvt_pk_f32_fp8(sfc.y, false),
-                                            __builtin_amdgcn_cvt_pk_f32_fp8(sfc.y, true)};
-                float acc = 0.0f;
-#pragma unroll
-                for (int k = 0; k < kCpl; ++k) {
-                    const int u = rr * kCpl + k;
-                    const float2_t sf = sfk[k];
-                    const uint4_t a = abuf[u];
-                    const float lo = dot_block(a.x, a.y, bp[k][0], bp[k][1]);
-                    const float hi = dot_block(a.z, a.w, bp[k][2], bp[k][3]);
-                    const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc));
-                    acc = live[k] ? nacc : acc;
-                    // refill the slot only after its last use: a load hoisted above
-                    // the use would need a second register set and copies that wait
-                    __builtin_amdgcn_sched_barrier(0);
-                    abuf[u] = load_a(arsrc, ro_refill + choff[k]);
-                }
-                const float v = group_sum<RED>(acc);
-                if (leader && q < nq) {
-                    float *dst = part + q * WPG + wig;
-                    *dst = first ? v : *dst + v;
-                }
+                decode_sfa(sfc, sfk);
             }
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kCpl; ++k) {
+                const int u = rr * kCpl + k;
+                const uint4_t a = abuf[u];
+                const float lo = dot_block(a.x, a.y, bp[k][0], bp[k][1]);
+                const float hi = dot_block(a.z, a.w, bp[k][2], bp[k][3]);
+                if (SCALED) {
+                    const float nacc = __builtin_fmaf(hi, sfk[k].y, __builtin_fmaf(lo, sfk[k].x, acc));
+                    acc = live[k] ? nacc : acc;
+                } else {
+                    // computed here, as the data arrives, not sunk to their use
+                    // after the staged scales
+                    float l2 = lo, h2 = hi;
+                    asm volatile("" : "+v"(l2), "+v"(h2));
+                    bsum[rr][k] = (float2_t){l2, h2};
+                }
+                // refill the slot only after its last use: a load hoisted above
+                // the use would need a second register set and copies that wait
+                __builtin_amdgcn_sched_barrier(0);
+                abuf[u] = load_a(arsrc, ro_refill + choff[k]);
+            }
+            if (SCALED)
+                store_row(grp + G * n, acc);
+        };
+
+        // rounds 0 .. PR-1: straight-line code, block sums kept
+#pragma unroll
+        for (int rr = 0; rr < PR; ++rr)
+            round(std::false_type{}, rr, rr);
+
+        // publish the staged scales, then finish the first rounds
+        stage_write();
+        __syncthreads();
+#pragma unroll
+        for (int rr = 0; rr < PR; ++rr) {
+            float2_t sfk[kCpl];
+            decode_sfa(sfa_of(rr), sfk);
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kCpl; ++k) {
+                const float nacc = __builtin_fmaf(bsum[rr][k].y, sfk[k].y, __builtin_fmaf(bsum[rr][k].x, sfk[k].x, acc));
+                acc = live[k] ? nacc : acc;
+            }
+            store_row(grp + G * rr, acc);
+        }
+
+        // the remaining rounds; at the loop entry the youngest loads are A
+        // loads, as on the loop's back edge, so its waits stay exact
+        sf_next = sfa_of(PR);
+        for (int32_t n0 = PR; n0 < NR; n0 += PR) {
+#pragma unroll
+            for (int rr = 0; rr < PR; ++rr)
+                round(std::true_type{}, n0 + rr, rr);
         }
     }
     __syncthreads();
@@ -428,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     // ---- per-row totals: add the per-wave sums in a fixed order, round once
     if (!SPLIT) {
         for (int32_t q = tid; q < nq; q += kThreads) {
-            const int32_t r = slot_row(slot0, q);
+            const int32_t r = slot_row(first, q);
             if (r < M) {
                 float v = part[q * WPG];
 #pragma unroll
@@ -448,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     // ticket is taken. Agent-scope fences are avoided on purpose: on this chip
     // they write back and invalidate the whole L2 of the XCD, once per workgroup.
     for (int32_t q = tid; q < nq; q += kThreads) {
-        const int32_t r = slot_row(slot0, q);
+        const int32_t r = slot_row(first, q);
         if (r < M) {
             float v = part[q * WPG];
 #pragma unroll
@@ -473,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     if (!is_last)
         return;
     for (int32_t q = tid; q < nq; q += kThreads) {
-        const int32_t r = slot_row(slot0, q);
+        const int32_t r = slot_row(first, q);
         if (r < M) {
             const float *pp = p.partials + (abatch + r) * p.S;
             float v = 0.0f;
@@ -491,7 +561,7 @@ struct Plan {
     int S;
     int kc_split;         // chunks per K-slice
     int P;                // workgroups per (batch, slice)
-    int spw;              // slots per workgroup
+    int spw;              // slots per workgroup (at most)
     int ns;               // slots per batch
     int segb;             // LDS bytes per staged scale row
     int wide_plain;
@@ -569,9 +639,31 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
     pl.lpr = choose_lpr(kc);
     pl.segb = seg_bytes(pl.lpr);
 
+    // Slots per workgroup: tiles never straddle a batch, so a batch has
+    // P = ceil(ns / spw) workgroups. Among grids of at most k * kTargetWGs
+    // workgroups (k = 1, 2, ...), take the one whose busiest CU holds the
+    // fewest slots (ceil(grid / 256) workgroups of spw slots), then the
+    // smaller grid: e.g. 258 workgroups would leave two CUs with twice the work.
     const int64_t spw_max = std::max<int64_t>(1, kSfaLdsBudget / (4 * pl.segb));
-    int64_t spw = total_slots >= kTargetWGs ? cdiv(total_slots, kTargetWGs) : 1;
-    spw = std::min(spw, spw_max);
+    int64_t spw = 1;
+    if (total_slots >= kTargetWGs) {
+        int64_t best_cost = INT64_MAX, best_grid = INT64_MAX;
+        for (int64_t k = 1; k <= 8; ++k) {
+            const int64_t per_batch = std::max<int64_t>(1, k * kTargetWGs / L);
+            const int64_t cand = cdiv(pl.ns, per_batch);
+            if (cand > spw_max)
+                continue;
+            const int64_t grid = L * S * cdiv(pl.ns, cand);
+            const int64_t cost = cdiv(grid, kTargetWGs) * cand;
+            if (cost < best_cost || (cost == best_cost && grid < best_grid)) {
+                best_cost = cost;
+                best_grid = grid;
+                spw = cand;
+            }
+        }
+        if (best_cost == INT64_MAX)
+            spw = spw_max;
+    }
     pl.spw = (int)spw;
     pl.P = (int)cdiv(pl.ns, spw);
     pl.n_wg = (int64_t)pl.P * L * S;

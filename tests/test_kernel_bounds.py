@@ -33,8 +33,8 @@ def xcd_remap(i, n):
     return x * q + np.minimum(x, r) + j
 
 
-def slot_row(slot0, q):
-    s = slot0 + (q >> 2)
+def slot_row(first, q):
+    s = first + (q >> 2)
     return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31)
 
 
@@ -92,67 +92,80 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
         s, t2 = lid % S, lid // S
         tile, l = t2 % P, t2 // P
         assert l < L
-        slot0 = tile * spw
-        nslots = min(spw, ns - slot0)
+        first = tile * spw
+        nslots = min(spw, ns - first)
         assert nslots >= 1
         nq = 4 * nslots
         assert nq * segb + nq * WPG * 4 <= lds_bytes
         c_begin, c_end = s * kc, min(s * kc + kc, nchunks)
         assert c_end > c_begin
-        row_base = (slot0 >> 5) << 7
+        row_base = (first >> 5) << 7
         a_begin = (l * M + row_base) * (K // 2)
         num_records = min(a_bytes - a_begin, 2 ** 31 - 1)
         nsteps = cdiv(nq, G) * CPL
-        rows_all = slot_row(slot0, np.arange(nq))
+        rows_all = slot_row(first, np.arange(nq))
         for c0 in range(c_begin, c_end, SEG):
             nck = min(SEG, c_end - c0)
             # ---- A: every step, including the prefetch issued past the end
             last = cdiv(nsteps, PREFETCH) * PREFETCH + PREFETCH
             for t in range(last):
                 q = np.minimum(grp + G * (t // CPL), nq - 1)
-                r = np.minimum(slot_row(slot0, q), M - 1)
+                r = np.minimum(slot_row(first, q), M - 1)
                 ci = c0 + np.minimum(j + (t % CPL) * lpr, nck - 1)
                 off = (r - row_base) * (K // 2) + ci * 16
                 assert off.min() >= 0 and (off + 16).max() <= num_records, "A read outside the resource"
-            # ---- staging: LDS byte -> global scale byte
+            # ---- staging through a buffer resource based at the workgroup's
+            # first scale byte: STAGE_MAX 16-byte loads per thread, issued after
+            # the A prefetch and written to LDS after rounds 0..PR-1 (which keep
+            # block sums and read the scales only after the barrier); a load
+            # past the items gets an out-of-range offset (reads zero).
+            direct = layout == 0 and not wide_plain
+            sfa_base = (first >> 5) * ncb * 512 if layout == 1 else row_base * nkb
+            s_records = min(sfa_batch - sfa_base, 2 ** 31 - 1)
+            assert s_records < 0x80000000
             dst_all, src_all = [], []
             if layout == 1:
                 ncb_seg, cb0 = (nck + 1) >> 1, c0 >> 1
                 items = nslots * ncb_seg
-                assert items <= STAGE_MAX * THREADS, "staging items not covered"
-                it = np.arange(items)
-                sl, cb = it % nslots, it // nslots
-                sg = slot0 + sl
-                src = l * sfa_batch + ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
-                assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
-                p0, p1 = pair_slot(2 * cb, lpr, CPL), pair_slot(2 * cb + 1, lpr, CPL)
-                for i4 in range(4):
-                    row = (sl * 4 + i4) * segb
-                    assert (row + 2 * np.maximum(p0, p1) + 2).max() <= nq * segb
-                    for b in range(2):
-                        dst_all += [row + 2 * p0 + b, row + 2 * p1 + b]
-                        src_all += [src + 4 * i4 + b, src + 4 * i4 + 2 + b]
-            elif wide_plain:
+            elif not direct:
                 units = nck >> 3
                 assert nck % 8 == 0
                 items = nq * units
-                assert items <= STAGE_MAX * THREADS, "staging items not covered"
-                it = np.arange(items)
-                q, u = it // units, it % units
-                r = np.minimum(slot_row(slot0, q), M - 1)
-                src = l * sfa_batch + r * nkb + 2 * c0 + 16 * u
-                assert (2 * c0 + 16 * u + 16).max() <= nkb
-                assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
-                for h in range(8):
-                    dst = q * segb + 2 * pair_slot(8 * u + h, lpr, CPL)
-                    assert (dst + 2).max() <= nq * segb
-                    for b in range(2):
-                        dst_all.append(dst + b)
-                        src_all.append(src + 2 * h + b)
             else:
+                items = 0
+            assert items <= STAGE_MAX * THREADS, "staging items not covered"
+            if items:
+                it = np.arange(items)
+                if layout == 1:
+                    sl, cb = it % nslots, it // nslots
+                    sg = first + sl
+                    off = (((sg >> 5) - (first >> 5)) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
+                    assert off.min() >= 0 and (off + 16).max() <= s_records, "SFA read outside the resource"
+                    src = l * sfa_batch + sfa_base + off
+                    p0, p1 = pair_slot(2 * cb, lpr, CPL), pair_slot(2 * cb + 1, lpr, CPL)
+                    for i4 in range(4):
+                        row = (sl * 4 + i4) * segb
+                        assert (row + 2 * np.maximum(p0, p1) + 2).max() <= nq * segb
+                        for b in range(2):
+                            dst_all += [row + 2 * p0 + b, row + 2 * p1 + b]
+                            src_all += [src + 4 * i4 + b, src + 4 * i4 + 2 + b]
+                else:
+                    q, u = it // units, it % units
+                    r = np.minimum(slot_row(first, q), M - 1)
+                    assert (2 * c0 + 16 * u + 16).max() <= nkb
+                    off = (r - row_base) * nkb + 2 * c0 + 16 * u
+                    assert off.min() >= 0 and (off + 16).max() <= s_records, "SFA read outside the resource"
+                    src = l * sfa_batch + sfa_base + off
+                    for h in range(8):
+                        dst = q * segb + 2 * pair_slot(8 * u + h, lpr, CPL)
+                        assert (dst + 2).max() <= nq * segb
+                        for b in range(2):
+                            dst_all.append(dst + b)
+                            src_all.append(src + 2 * h + b)
+            if direct:
                 it = np.arange(nq * nck)
                 q, c = it // nck, it % nck
-                r = np.minimum(slot_row(slot0, q), M - 1)
+                r = np.minimum(slot_row(first, q), M - 1)
                 src = l * sfa_batch + r * nkb + 2 * (c0 + c)
                 assert src.min() >= 0 and (src + 2).max() <= L * sfa_batch
                 dst = q * segb + 2 * pair_slot(c, lpr, CPL)
@@ -160,6 +173,8 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                 for b in range(2):
                     dst_all.append(dst + b)
                     src_all.append(src + b)
+            dst_cat = np.concatenate(dst_all)
+            assert np.unique(dst_cat).size == dst_cat.size, "two items write one LDS byte"
             lds_src = np.full(nq * segb, -1, np.int64)
             lds_src[np.concatenate(dst_all)] = np.concatenate(src_all)
             # ---- b': B chunk and its two SFB scales

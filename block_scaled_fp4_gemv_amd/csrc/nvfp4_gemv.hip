@@ -55,13 +55,15 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;                 // compute waves per workgroup
+constexpr int kThreads = 64 * kWaves;     // compute threads
+constexpr int kBlock = kThreads + 64;     // plus one wave that stages the scales
 constexpr int kCpl = 4;                   // chunks per lane per K-segment
 constexpr int kPrefetch = 8;              // chunk loads in flight per lane (multiple of kCpl)
-constexpr int kMaxLpr = 256;              // lanes per row, at most the whole workgroup
+constexpr int kDeferRounds = 2;           // first row rounds that keep block sums (multiple of the ring's rounds)
+constexpr int kMaxLpr = 256;              // lanes per row, at most the compute threads
 constexpr int kSfaLdsBudget = 48 * 1024;  // staged scale bytes per workgroup
-constexpr int kStageMax = 12;             // 16-byte scale loads per thread (budget / 16 / threads)
+constexpr int kDmaBytes = 64 * 16;        // LDS bytes one wave-wide 16-byte direct-to-LDS load fills
 constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
 constexpr int kXcds = 8;                  // MI355X: 8 XCDs, WG ids dealt round-robin
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
@@ -70,8 +72,7 @@ constexpr int kCachePolicyNT = 2;         // buffer load cache policy: non-tempo
 constexpr int64_t kMaxK = INT64_C(1) << 22; // keeps one workgroup's A offsets below 2^31
 
 static_assert(kPrefetch % kCpl == 0, "a row's chunk-steps must not straddle the prefetch ring");
-static_assert(kCpl == 4, "one 8-byte LDS read carries a lane's scales of one row");
-static_assert(kStageMax * kThreads * 16 >= kSfaLdsBudget, "staging registers cover the LDS budget");
+static_assert(kDeferRounds % (kPrefetch / kCpl) == 0, "deferred rounds end on a ring boundary");
 
 struct Params {
     int32_t M, K, L;
@@ -80,7 +81,7 @@ struct Params {
     int32_t P;            // workgroups per (batch, slice)
     int32_t spw;          // slots per workgroup (at most)
     int32_t ns;           // slots per batch that hold at least one row
-    int32_t segb;         // LDS bytes per row of staged scales
+    int32_t stage_bytes;  // LDS bytes for the staged scales (whole direct-to-LDS loads)
     int32_t wide_plain;   // plain scales staged in 16-byte units
     int64_t sfa_batch;    // bytes per batch of SFA
     int64_t sfb_batch;    // bytes per batch of SFB
@@ -103,13 +104,6 @@ __device__ inline int32_t slot_row(int32_t first, int32_t q)
 {
     const int32_t s = first + (q >> 2);
     return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31);
-}
-
-// Pair slot of segment chunk c in a staged scale row: lane c % LPR, step c / LPR.
-template <int LPR>
-__device__ inline int32_t pair_slot(int32_t c)
-{
-    return (c % LPR) * kCpl + c / LPR;
 }
 
 // Byte offset of the two scales of chunk c (blocks 2c, 2c+1) of row r.
@@ -215,7 +209,7 @@ __device__ __attribute__((always_inline)) inline void make_bprime(uint4_t b, uin
 }
 
 template <int LAYOUT, int LPR, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
+__global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
     uint16_t *__restrict__ C, Params p)
@@ -224,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     constexpr int G = kThreads / LPR;            // row groups (rows in flight) per workgroup
     constexpr int WPG = LPR > 64 ? LPR / 64 : 1; // waves per row group
     constexpr int RED = LPR < 64 ? LPR : 64;     // lanes summed inside one wave
+    constexpr int PR = kPrefetch / kCpl;         // row rounds in the load ring
+    constexpr int DR = kDeferRounds;             // first rounds that keep their block sums
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -232,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     const int32_t tile = (int32_t)(t2 % (uint32_t)p.P);
     const int32_t l = (int32_t)(t2 / (uint32_t)p.P);
 
-    const int32_t M = p.M, K = p.K, segb = p.segb;
+    const int32_t M = p.M, K = p.K;
     const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
     // Slots of this workgroup: a contiguous range, so that its blocked scales
     // are few whole lines per 512-byte tile (neighbouring slots share a line).
@@ -242,7 +238,14 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     const int32_t c_begin = s * p.kc_split;
     const int32_t c_end = min(c_begin + p.kc_split, nchunks);
 
+    // Threads 0 .. kThreads-1 compute; the last wave only stages the scales.
+    // A wave's vector loads complete in order, so scale loads issued by a
+    // computing wave would hold back every later A load of that wave; issued
+    // by a wave of their own, they stream beside the A loads.
     const int tid = threadIdx.x;
+    // wave-uniform (scalar) so that the two roles are separate paths, not
+    // one path with two lane masks whose registers would all be live at once
+    const bool loader = __builtin_amdgcn_readfirstlane(tid) >= kThreads;
     const int grp = tid / LPR, j = tid % LPR;
     const int lane = tid & 63;
     const int wig = WPG > 1 ? j >> 6 : 0;                 // wave index inside the row group
@@ -252,11 +255,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
     const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
     const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
     const uint8_t *b_l = B + (int64_t)l * (K >> 1);
-    float *part = (float *)(lds + (size_t)nq * segb);      // [nq][WPG] per-wave row sums
+    uint8_t *stage = lds;                                  // staged scales of the segment
+    float *part = (float *)(lds + p.stage_bytes);          // [nq][WPG] per-wave row sums
 
     // A through a buffer resource based at the first row of this workgroup's
     // first 128-row block: 32-bit lane offsets (the rows of one workgroup lie
-    // within a few blocks), and lanes past the end of A read zero.
+    // within a few blocks).
     const int32_t row_base = (first >> 5) << 7;
     const int64_t a_begin = (abatch + row_base) * (int64_t)(K >> 1);
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -264,157 +268,105 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
         kBufferFlags);
 
     const int32_t NR = (nq + G - 1) / G;                   // row rounds per group
+    const bool direct = LAYOUT == NVFP4_SF_PLAIN && !p.wide_plain;
 
-    // The scales of the workgroup's rows and K-segment are staged into LDS with
-    // 16-byte loads issued after the first kPrefetch A loads, so that the first
-    // rows never wait for them: the first PR row rounds (the ones already in
-    // the load ring) keep their exact 16-element block sums in registers and
-    // apply the scales once the staged scales are published behind a barrier.
-    // The staging loads go through a buffer resource: a fixed number per thread
-    // keeps the wait counts of the A stream exact, and the unused ones get an
-    // out-of-range offset, which returns zero without a memory access.
-    constexpr int PR = kPrefetch / kCpl;               // rounds in the load ring
-    const int64_t sfa_base = LAYOUT == NVFP4_SF_BLOCKED ? (int64_t)(first >> 5) * ncb * 512
-                                                        : (int64_t)row_base * nkb;
-    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(sfa_l + sfa_base), (short)0,
-        (int)min(p.sfa_batch - sfa_base, (int64_t)0x7FFFFFFF), kBufferFlags);
+    // Staged layout (bytes of LDS): blocked: item (slot sl, 4-block group cb)
+    // = 16 bytes at (cb * nslots + sl) * 16, i.e. row 4 sl + i4 at +4 i4 and
+    // chunk c of the group (2 scales) at +2 (c & 1); plain: the 2 scales of
+    // (row q, chunk c) at (q * nck + c) * 2. Both roles pass the same barriers:
+    // per segment one after the previous segment's scales are read (not before
+    // the first) and one that publishes the staged scales; then the ones of
+    // the epilogue.
+    if (loader) {
+        for (int32_t c0 = c_begin; c0 < c_end; c0 += SEG) {
+            const int32_t nck = min(SEG, c_end - c0);
+            if (c0 != c_begin)
+                __syncthreads();                           // the previous segment's scales are read
+            const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1, units = nck >> 3;
+            if (!direct) {
+                // wave-wide direct-to-LDS load i puts item i*64 + lane at
+                // (i*64 + lane) * 16 (lanes past the items repeat the last
+                // item, inside the area); all loads are in flight at once
+                const int32_t items = LAYOUT == NVFP4_SF_BLOCKED ? nslots * ncb_seg : nq * units;
+                const int32_t nload = (items + 63) >> 6;
+                for (int32_t i = 0; i < nload; ++i) {
+                    const int32_t it = min(i * 64 + lane, items - 1);
+                    const uint8_t *src;
+                    if (LAYOUT == NVFP4_SF_BLOCKED) {
+                        const int32_t sg = first + it % nslots, cb = it / nslots;
+                        src = sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16;
+                    } else {
+                        const int32_t q = it / units, u = it % units;
+                        const int32_t r = min(slot_row(first, q), M - 1);
+                        src = sfa_l + (int64_t)r * nkb + 2 * c0 + 16 * u;
+                    }
+                    __builtin_amdgcn_global_load_lds((const void *)src,
+                                                     (__attribute__((address_space(3))) void *)(stage + i * kDmaBytes),
+                                                     16, 0, 0);
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the staged bytes are in LDS
+            } else {
+                // plain scales whose rows are not 16-byte multiples: 2 bytes at a time
+                for (int32_t it = lane; it < nq * nck; it += 64) {
+                    const int32_t q = it / nck, c = it % nck;
+                    const int32_t r = min(slot_row(first, q), M - 1);
+                    *(uint16_t *)(stage + 2 * it) = *(const uint16_t *)(sfa_l + (int64_t)r * nkb + 2 * (c0 + c));
+                }
+            }
+            __syncthreads();                               // publish the staged scales
+        }
+        __syncthreads();                                   // the epilogue's barriers
+        if (SPLIT) {
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
 
     for (int32_t c0 = c_begin; c0 < c_end; c0 += SEG) {
         const int32_t nck = min(SEG, c_end - c0);
         const bool first_seg = c0 == c_begin;
         if (!first_seg)
-            __syncthreads();                               // previous segment's LDS reads done
+            __syncthreads();                               // the previous segment's scales are read
 
-        // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
-        // the end read a clamped (valid) chunk so that every load is
-        // unconditional and the wait counts stay exact.
-        // Byte offsets into A: round n of the group reads row slot_row(q_n)
-        // (clamped to a real row); step k of a round reads the lane's chunk k
-        // (clamped to a real chunk; its contribution is masked by live[k]).
         auto row_off = [&](int32_t n) -> uint32_t {
             const int32_t q = min(grp + G * n, nq - 1);
             const int32_t r = min(slot_row(first, q), M - 1);
             return (uint32_t)(r - row_base) * (uint32_t)(K >> 1);
         };
+        // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
+        // the end read a clamped (valid) chunk so that every load is
+        // unconditional and the wait counts stay exact: round n of the group
+        // reads row slot_row(q_n) (clamped to a real row), step k the lane's
+        // chunk k (clamped to a real chunk; its contribution is masked by live[k]).
         uint32_t choff[kCpl];
+        uint32_t sfoff[kCpl];                              // staged-scale byte of chunk k, row part excluded
         bool live[kCpl];
 #pragma unroll
         for (int k = 0; k < kCpl; ++k) {
             const int32_t cl = j + k * LPR;
+            const int32_t cc = min(cl, nck - 1);
             live[k] = cl < nck;
-            choff[k] = (uint32_t)(c0 + min(cl, nck - 1)) * 16u;
+            choff[k] = (uint32_t)(c0 + cc) * 16u;
+            sfoff[k] = LAYOUT == NVFP4_SF_BLOCKED ? (uint32_t)((cc >> 1) * nslots * 16 + (cc & 1) * 2)
+                                                  : (uint32_t)(cc * 2);
         }
-
-        // ---- staging items. Blocked: item (slot, 4-block group) is one 16-byte
-        // vector = 4 rows x 4 blocks. Wide plain: item (row, 8 chunks) is 16
-        // contiguous bytes of a plain scale row. LDS layout: row q holds, for
-        // each lane j of a row group, the 2*kCpl scale bytes of its chunks j,
-        // j+LPR, ... (chunk c at pair slot (c % LPR) * kCpl + c / LPR), so one
-        // 8-byte read gives a lane all the scales of a row.
-        const bool direct = LAYOUT == NVFP4_SF_PLAIN && !p.wide_plain;
-        const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1, units = nck >> 3;
-        const int32_t items = LAYOUT == NVFP4_SF_BLOCKED ? nslots * ncb_seg : (direct ? 0 : nq * units);
-        uint4_t sv[kStageMax];
-        auto stage_load = [&]() {
-#pragma unroll
-            for (int i = 0; i < kStageMax; ++i) {
-                const int32_t it = tid + i * kThreads;
-                uint32_t off = 0x80000000u;
-                if (LAYOUT == NVFP4_SF_BLOCKED) {
-                    const int32_t sg = first + it % nslots, cb = it / nslots;
-                    if (it < items)
-                        off = (uint32_t)((((sg >> 5) - (first >> 5)) * ncb + cb0 + cb) * 512 + (sg & 31) * 16);
-                } else {
-                    const int32_t q = it / max(units, 1), u = it % max(units, 1);
-                    const int32_t r = min(slot_row(first, min(q, nq - 1)), M - 1);
-                    if (it < items)
-                        off = (uint32_t)((r - row_base) * nkb + 2 * c0 + 16 * u);
-                }
-                sv[i] = __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)off, 0, 0);
-            }
-            // keep every load here: a load sunk into the conditional writes
-            // below would be waited for together with the whole load ring
-            asm volatile("" ::: "memory");
-        };
-        auto stage_write = [&]() {
-            // recompute the item indices here instead of keeping those of the
-            // loads alive across the first rounds
-            int32_t t = tid;
-            asm volatile("" : "+v"(t));
-#pragma unroll
-            for (int i = 0; i < kStageMax; ++i) {
-                const int32_t it = t + i * kThreads;
-                if (it >= items)
-                    break;
-                const uint32_t w4[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
-                if (LAYOUT == NVFP4_SF_BLOCKED) {
-                    const int32_t sl = it % nslots, cb = it / nslots;
-                    uint8_t *row0 = lds + (size_t)(sl * 4) * segb;     // rows i4 = 0..3
-                    const int32_t p0 = pair_slot<LPR>(2 * cb), p1 = pair_slot<LPR>(2 * cb + 1);
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                        *(uint16_t *)(row0 + i4 * segb + 2 * p0) = (uint16_t)w4[i4];
-                        *(uint16_t *)(row0 + i4 * segb + 2 * p1) = (uint16_t)(w4[i4] >> 16);
-                    }
-                } else {
-                    const int32_t q = it / units, u = it % units;
-                    uint8_t *row = lds + (size_t)q * segb;         // chunks 8u .. 8u+7
-#pragma unroll
-                    for (int h = 0; h < 8; ++h)
-                        *(uint16_t *)(row + 2 * pair_slot<LPR>(8 * u + h)) = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
-                }
-            }
-        };
-
-        // Loads are issued in this order: B and SFB for b', the first kPrefetch
-        // steps of A, the staged scales. Vector loads complete in order, so
-        // each consumer waits only for its own loads and the ones before them.
-        uint4_t abuf[kPrefetch];
-        uint4_t bload[kCpl];
-        uint32_t sload[kCpl];
-#pragma unroll
-        for (int k = 0; k < kCpl; ++k) {
-            const int32_t ci = c0 + min(j + k * LPR, nck - 1);
-            bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
-            sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < kPrefetch; ++u)
-            abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_load();
-        __builtin_amdgcn_sched_barrier(0);
-
-        if (direct) {
-            // item (row, chunk): the two scales of one chunk, copied directly
-            for (int32_t it = tid; it < nq * nck; it += kThreads) {
-                const int32_t q = it / nck, c = it % nck;
-                const int32_t r = min(slot_row(first, q), M - 1);
-                *(uint16_t *)(lds + (size_t)q * segb + 2 * pair_slot<LPR>(c)) =
-                    *(const uint16_t *)(sfa_l + (int64_t)r * nkb + 2 * (c0 + c));
-            }
-        }
-
-        // ---- b' for this lane's chunks of the segment (registers, reused for every row)
-        uint4_t bp[kCpl][4];
-#pragma unroll
-        for (int k = 0; k < kCpl; ++k)
-            make_bprime(bload[k], sload[k], bp[k]);
-
-        // ---- the group's rows one after another, kPrefetch chunk loads ahead.
-        // A round is one row: kCpl steps, one 16-byte chunk each. The scales of
-        // the next round are read from LDS one round early.
-        auto sfa_of = [&](int32_t n) -> uint2_t {
+        auto sfa_of = [&](int32_t n) -> uint4_t {         // the lane's 4 scale pairs of round n
             const int32_t q = min(grp + G * n, nq - 1);
-            return *(const uint2_t *)(lds + (size_t)q * segb + j * (2 * kCpl));
+            const uint32_t rowpart = LAYOUT == NVFP4_SF_BLOCKED ? (uint32_t)((q >> 2) * 16 + (q & 3) * 4)
+                                                                : (uint32_t)(q * nck * 2);
+            uint4_t w;
+            w.x = *(const uint16_t *)(stage + sfoff[0] + rowpart);
+            w.y = *(const uint16_t *)(stage + sfoff[1] + rowpart);
+            w.z = *(const uint16_t *)(stage + sfoff[2] + rowpart);
+            w.w = *(const uint16_t *)(stage + sfoff[3] + rowpart);
+            return w;
         };
-        auto decode_sfa = [&](uint2_t w, float2_t (&sfk)[kCpl]) {
+        auto decode_sfa = [&](uint4_t w, float2_t (&sfk)[kCpl]) {
             sfk[0] = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false);
-            sfk[1] = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
-            sfk[2] = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false);
-            sfk[3] = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+            sfk[1] = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false);
+            sfk[2] = __builtin_amdgcn_cvt_pk_f32_fp8(w.z, false);
+            sfk[3] = __builtin_amdgcn_cvt_pk_f32_fp8(w.w, false);
         };
         auto store_row = [&](int32_t q, float acc) {
             const float v = group_sum<RED>(acc);
@@ -423,17 +375,19 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
                 *dst = first_seg ? v : *dst + v;
             }
         };
+        uint4_t abuf[kPrefetch];
+        uint4_t bp[kCpl][4];
+        float2_t bsum[DR][kCpl];                           // block sums of the first rounds
+        uint4_t sf_next = {0u, 0u, 0u, 0u};
         // One round: block sums of the lane's chunks against b', then (SCALED)
         // the scales, the row sum and its store; the ring slot is refilled with
         // the step PR rounds ahead.
-        float2_t bsum[PR][kCpl];                         // block sums of the first rounds
-        uint2_t sf_next = {0u, 0u};
-        auto round = [&](auto scaled, int32_t n, int rr) {
+        auto round = [&](auto scaled, int32_t n, int rr, int dn) {
             constexpr bool SCALED = decltype(scaled)::value;
             const uint32_t ro_refill = row_off(n + PR);
             float2_t sfk[kCpl];
             if (SCALED) {
-                const uint2_t sfc = sf_next;
+                const uint4_t sfc = sf_next;
                 sf_next = sfa_of(n + 1);
                 decode_sfa(sfc, sfk);
             }
@@ -452,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
                     // after the staged scales
                     float l2 = lo, h2 = hi;
                     asm volatile("" : "+v"(l2), "+v"(h2));
-                    bsum[rr][k] = (float2_t){l2, h2};
+                    bsum[dn][k] = (float2_t){l2, h2};
                 }
                 // refill the slot only after its last use: a load hoisted above
                 // the use would need a second register set and copies that wait
@@ -463,34 +417,51 @@ __global__ __launch_bounds__(kThreads) void nvfp4_gemv_kernel(
                 store_row(grp + G * n, acc);
         };
 
-        // rounds 0 .. PR-1: straight-line code, block sums kept
+        // ---- B and SFB for b', then the first kPrefetch steps of A
+        uint4_t bload[kCpl];
+        uint32_t sload[kCpl];
 #pragma unroll
-        for (int rr = 0; rr < PR; ++rr)
-            round(std::false_type{}, rr, rr);
+        for (int k = 0; k < kCpl; ++k) {
+            const int32_t ci = c0 + min(j + k * LPR, nck - 1);
+            bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
+            sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kPrefetch; ++u)
+            abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
+        __builtin_amdgcn_sched_barrier(0);
+        // b' for this lane's chunks of the segment (registers, reused for every row)
+#pragma unroll
+        for (int k = 0; k < kCpl; ++k)
+            make_bprime(bload[k], sload[k], bp[k]);
+        // rounds 0 .. DR-1 keep their block sums (straight-line code)
+#pragma unroll
+        for (int n = 0; n < DR; ++n)
+            round(std::false_type{}, n, n % PR, n);
 
-        // publish the staged scales, then finish the first rounds
-        stage_write();
-        __syncthreads();
+        __syncthreads();                                   // the staged scales are published
+
+        // finish the first rounds, then the rest with the scales read one round ahead
 #pragma unroll
-        for (int rr = 0; rr < PR; ++rr) {
+        for (int n = 0; n < DR; ++n) {
             float2_t sfk[kCpl];
-            decode_sfa(sfa_of(rr), sfk);
+            decode_sfa(sfa_of(n), sfk);
             float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < kCpl; ++k) {
-                const float nacc = __builtin_fmaf(bsum[rr][k].y, sfk[k].y, __builtin_fmaf(bsum[rr][k].x, sfk[k].x, acc));
+                const float nacc = __builtin_fmaf(bsum[n][k].y, sfk[k].y, __builtin_fmaf(bsum[n][k].x, sfk[k].x, acc));
                 acc = live[k] ? nacc : acc;
             }
-            store_row(grp + G * rr, acc);
+            store_row(grp + G * n, acc);
         }
-
-        // the remaining rounds; at the loop entry the youngest loads are A
-        // loads, as on the loop's back edge, so its waits stay exact
-        sf_next = sfa_of(PR);
-        for (int32_t n0 = PR; n0 < NR; n0 += PR) {
+        // at the loop entry the youngest loads are A loads, as on the loop's
+        // back edge, so its waits stay exact
+        sf_next = sfa_of(DR);
+        for (int32_t n0 = DR; n0 < NR; n0 += PR) {
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr)
-                round(std::true_type{}, n0 + rr, rr);
+                round(std::true_type{}, n0 + rr, rr, 0);
         }
     }
     __syncthreads();
@@ -563,7 +534,7 @@ struct Plan {
     int P;                // workgroups per (batch, slice)
     int spw;              // slots per workgroup (at most)
     int ns;               // slots per batch
-    int segb;             // LDS bytes per staged scale row
+    int stage_bytes;      // LDS bytes of staged scales
     int wide_plain;
     int64_t n_wg;
     int lds_bytes;
@@ -598,12 +569,11 @@ int choose_lpr(int64_t nc)
     return std::min<int>(kMaxLpr, pow2_ceil(cdiv(nc, kCpl)));
 }
 
-// LDS bytes per staged scale row: 2 bytes per chunk of the segment. The groups
-// of one wave read consecutive rows, 2*kCpl bytes per lane, i.e. one
-// contiguous run of LDS.
-int seg_bytes(int lpr)
+// LDS bytes of staged scales for spw slots: at most 2*lpr 16-byte items per
+// slot and segment (2 bytes per row and chunk), in whole direct-to-LDS loads.
+int stage_bytes(int lpr, int64_t spw)
 {
-    return (int)align_up((size_t)(2 * kCpl * lpr), 16);
+    return (int)align_up((size_t)(32 * lpr * spw), kDmaBytes);
 }
 
 nvfp4_status_t check_shape(int64_t M, int64_t K, int64_t L)
@@ -637,14 +607,13 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
     pl.S = (int)S;
     pl.kc_split = (int)kc;
     pl.lpr = choose_lpr(kc);
-    pl.segb = seg_bytes(pl.lpr);
 
     // Slots per workgroup: tiles never straddle a batch, so a batch has
     // P = ceil(ns / spw) workgroups. Among grids of at most k * kTargetWGs
     // workgroups (k = 1, 2, ...), take the one whose busiest CU holds the
     // fewest slots (ceil(grid / 256) workgroups of spw slots), then the
     // smaller grid: e.g. 258 workgroups would leave two CUs with twice the work.
-    const int64_t spw_max = std::max<int64_t>(1, kSfaLdsBudget / (4 * pl.segb));
+    const int64_t spw_max = std::max<int64_t>(1, kSfaLdsBudget / (32 * pl.lpr));
     int64_t spw = 1;
     if (total_slots >= kTargetWGs) {
         int64_t best_cost = INT64_MAX, best_grid = INT64_MAX;
@@ -668,7 +637,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
     pl.P = (int)cdiv(pl.ns, spw);
     pl.n_wg = (int64_t)pl.P * L * S;
     const int wpg = pl.lpr > 64 ? pl.lpr / 64 : 1;
-    pl.lds_bytes = (int)(4 * spw * pl.segb + 4 * spw * wpg * (int)sizeof(float));
+    pl.stage_bytes = stage_bytes(pl.lpr, spw);
+    pl.lds_bytes = (int)(pl.stage_bytes + 4 * spw * wpg * (int)sizeof(float));
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
     if (S > 1) {
         pl.ws_partials = align_up((size_t)(L * M * S) * sizeof(float), kWsAlign);
@@ -683,7 +653,7 @@ template <int LAYOUT, int LPR>
 hipError_t launch_lpr(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                       void *c, const Params &p, hipStream_t st)
 {
-    const dim3 grid((uint32_t)pl.n_wg), block(kThreads);
+    const dim3 grid((uint32_t)pl.n_wg), block(kBlock);
     if (pl.S > 1)
         hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, true>), grid, block, pl.lds_bytes, st,
                            (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
@@ -742,7 +712,7 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
     p.P = pl.P;
     p.spw = pl.spw;
     p.ns = pl.ns;
-    p.segb = pl.segb;
+    p.stage_bytes = pl.stage_bytes;
     p.wide_plain = pl.wide_plain;
     p.a_bytes = L * M * (K / 2);
     const int64_t nkb = K / 16, ncb = cdiv(nkb, 4);
@@ -866,7 +836,7 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
     plan->k_splits = pl.S;
     plan->k_per_split = pl.kc_split * 32;
     plan->workgroups = pl.n_wg;
-    plan->threads_per_wg = kThreads;
+    plan->threads_per_wg = kBlock;
     plan->lds_bytes = pl.lds_bytes;
     return NVFP4_OK;
 }

@@ -104,7 +104,7 @@ def test_plans(w):
     tiles = synth.ceil_div(ns, p["rows_per_wg"] // 4)
     assert p["workgroups"] == tiles * w.L * p["k_splits"]
     assert p["lds_bytes"] <= 64 * 1024
-    assert p["threads_per_wg"] == 256
+    assert p["threads_per_wg"] == 320          # 4 computing waves and the staging wave
 
 
 def test_long_k_is_segmented_not_split():

@@ -4,15 +4,14 @@ This mirrors the index arithmetic of nvfp4_gemv.hip for the whole grid of each
 tested shape, using the launch plan the library reports, and checks:
   * every A, B, SFA and SFB read is inside its buffer (A through a buffer
     resource: inside the resource's byte range),
-  * the scales staged into LDS are exactly the ones the compute reads for every
-    real (row, chunk): the staging and the read side agree byte for byte, and
-    no real row reads padding of the blocked layout,
-  * every staging item is covered by the fixed number of loads per thread, and
-    LDS offsets stay inside the allocation,
+  * the staging wave's LDS writes stay inside the staging area, no two of them
+    hit one byte, and the scales the computing waves read for every real
+    (row, chunk) are exactly the ones staged there, byte for byte; no real row
+    reads padding of the blocked layout,
   * every output row is written exactly once, and split-K partial and ticket
     indices stay inside the workspace.
-Keep it in step with the kernel's constants: 256 threads, 4 chunks per lane,
-8 chunk loads in flight, 12 staging loads per thread, 1024 tickets.
+Keep it in step with the kernel's constants: 4 computing waves and one staging
+wave, 4 chunks per lane, 8 chunk loads in flight, 1024 tickets.
 """
 import numpy as np
 import pytest
@@ -20,7 +19,9 @@ import pytest
 import block_scaled_fp4_gemv_amd as g
 import synth
 
-THREADS, CPL, PREFETCH, STAGE_MAX, XCDS, MAX_TICKETS = 256, 4, 8, 12, 8, 1024
+THREADS, CPL, PREFETCH, XCDS, MAX_TICKETS = 256, 4, 8, 8, 1024
+LOADER = 64                 # threads of the staging wave
+DMA_BYTES = 64 * 16         # LDS bytes one wave-wide staging load fills
 
 
 def cdiv(a, b):
@@ -38,13 +39,8 @@ def slot_row(first, q):
     return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31)
 
 
-def seg_bytes(lpr, cpl=CPL):
-    return cdiv(2 * cpl * lpr, 16) * 16
-
-
-def pair_slot(c, lpr, cpl=CPL):
-    """Pair slot of segment chunk c in a staged scale row (lane c % lpr, step c / lpr)."""
-    return (c % lpr) * cpl + c // lpr
+def stage_bytes(lpr, spw):
+    return cdiv(32 * lpr * spw, DMA_BYTES) * DMA_BYTES
 
 
 def sf_offset(layout, r, kb, nkb, ncb):
@@ -55,25 +51,26 @@ def sf_offset(layout, r, kb, nkb, ncb):
 
 
 def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREADS, cpl=CPL,
-                prefetch=PREFETCH, stage_max=STAGE_MAX, max_tickets=MAX_TICKETS):
+                prefetch=PREFETCH, max_tickets=MAX_TICKETS):
     """Walk the whole grid of one launch. ``plan``/``workspace_bytes`` default
     to the built library's; the constants can be overridden to check a variant."""
-    THREADS, CPL, PREFETCH, STAGE_MAX = threads, cpl, prefetch, stage_max
+    THREADS, CPL, PREFETCH = threads, cpl, prefetch
     p = (plan or g.nvfp4_gemv_plan)(M, K, L)
     ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
     lpr, spw, S = p["lanes_per_row"], p["rows_per_wg"] // 4, p["k_splits"]
     kc, n_wg, lds_bytes = p["k_per_split"] // 32, p["workgroups"], p["lds_bytes"]
-    assert p["threads_per_wg"] == THREADS
+    assert p["threads_per_wg"] == THREADS + LOADER
     nchunks, nkb = K // 32, K // 16
     ncb = cdiv(nkb, 4)
     ns = 32 * (M // 128) + min(32, M % 128)
     P = cdiv(ns, spw)
     assert n_wg == P * L * S
     SEG, G, WPG = lpr * CPL, THREADS // lpr, max(1, lpr // 64)
-    segb = seg_bytes(lpr, CPL)
-    assert lds_bytes == 4 * spw * segb + 4 * spw * WPG * 4
+    stb = stage_bytes(lpr, spw)
+    assert lds_bytes == stb + 4 * spw * WPG * 4
     assert lds_bytes <= 64 * 1024
     wide_plain = nchunks % 8 == 0 and kc % 8 == 0
+    direct = layout == 0 and not wide_plain
     a_bytes, b_size = L * M * K // 2, L * K // 2
     sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512
     sfb_batch = nkb if layout == 0 else ncb * 512
@@ -88,6 +85,7 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     assert np.array_equal(np.sort(lids), np.arange(n_wg)), "remap is not a bijection"
     tid = np.arange(THREADS)
     grp, j = tid // lpr, tid % lpr
+    lane = np.arange(LOADER)
     for lid in lids:
         s, t2 = lid % S, lid // S
         tile, l = t2 % P, t2 // P
@@ -96,7 +94,7 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
         nslots = min(spw, ns - first)
         assert nslots >= 1
         nq = 4 * nslots
-        assert nq * segb + nq * WPG * 4 <= lds_bytes
+        assert stb + nq * WPG * 4 <= lds_bytes
         c_begin, c_end = s * kc, min(s * kc + kc, nchunks)
         assert c_end > c_begin
         row_base = (first >> 5) << 7
@@ -114,69 +112,42 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                 ci = c0 + np.minimum(j + (t % CPL) * lpr, nck - 1)
                 off = (r - row_base) * (K // 2) + ci * 16
                 assert off.min() >= 0 and (off + 16).max() <= num_records, "A read outside the resource"
-            # ---- staging through a buffer resource based at the workgroup's
-            # first scale byte: STAGE_MAX 16-byte loads per thread, issued after
-            # the A prefetch and written to LDS after rounds 0..PR-1 (which keep
-            # block sums and read the scales only after the barrier); a load
-            # past the items gets an out-of-range offset (reads zero).
-            direct = layout == 0 and not wide_plain
-            sfa_base = (first >> 5) * ncb * 512 if layout == 1 else row_base * nkb
-            s_records = min(sfa_batch - sfa_base, 2 ** 31 - 1)
-            assert s_records < 0x80000000
-            dst_all, src_all = [], []
-            if layout == 1:
-                ncb_seg, cb0 = (nck + 1) >> 1, c0 >> 1
-                items = nslots * ncb_seg
-            elif not direct:
-                units = nck >> 3
-                assert nck % 8 == 0
-                items = nq * units
+            # ---- staging wave: LDS byte -> global scale byte
+            ncb_seg, cb0, units = (nck + 1) >> 1, c0 >> 1, nck >> 3
+            lds_src = np.full(stb, -1, np.int64)
+            if not direct:
+                items = nslots * ncb_seg if layout == 1 else nq * units
+                assert layout == 1 or nck % 8 == 0
+                nload = cdiv(items, 64)
+                dst_all, src_all = [], []
+                for i in range(nload):
+                    it = np.minimum(i * 64 + lane, items - 1)
+                    if layout == 1:
+                        sg, cb = first + it % nslots, it // nslots
+                        src = ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
+                    else:
+                        q, u = it // units, it % units
+                        r = np.minimum(slot_row(first, q), M - 1)
+                        assert (2 * c0 + 16 * u + 16).max() <= nkb
+                        src = r * nkb + 2 * c0 + 16 * u
+                    assert src.min() >= 0 and (src + 16).max() <= sfa_batch, "SFA read outside the batch"
+                    dst = i * DMA_BYTES + lane * 16
+                    assert (dst + 16).max() <= stb, "staged item outside the staging area"
+                    for b in range(16):
+                        dst_all.append(dst + b)
+                        src_all.append(l * sfa_batch + src + b)
+                dst_cat = np.concatenate(dst_all)
+                assert np.unique(dst_cat).size == dst_cat.size, "two staging lanes write one LDS byte"
+                lds_src[dst_cat] = np.concatenate(src_all)
             else:
-                items = 0
-            assert items <= STAGE_MAX * THREADS, "staging items not covered"
-            if items:
-                it = np.arange(items)
-                if layout == 1:
-                    sl, cb = it % nslots, it // nslots
-                    sg = first + sl
-                    off = (((sg >> 5) - (first >> 5)) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
-                    assert off.min() >= 0 and (off + 16).max() <= s_records, "SFA read outside the resource"
-                    src = l * sfa_batch + sfa_base + off
-                    p0, p1 = pair_slot(2 * cb, lpr, CPL), pair_slot(2 * cb + 1, lpr, CPL)
-                    for i4 in range(4):
-                        row = (sl * 4 + i4) * segb
-                        assert (row + 2 * np.maximum(p0, p1) + 2).max() <= nq * segb
-                        for b in range(2):
-                            dst_all += [row + 2 * p0 + b, row + 2 * p1 + b]
-                            src_all += [src + 4 * i4 + b, src + 4 * i4 + 2 + b]
-                else:
-                    q, u = it // units, it % units
-                    r = np.minimum(slot_row(first, q), M - 1)
-                    assert (2 * c0 + 16 * u + 16).max() <= nkb
-                    off = (r - row_base) * nkb + 2 * c0 + 16 * u
-                    assert off.min() >= 0 and (off + 16).max() <= s_records, "SFA read outside the resource"
-                    src = l * sfa_batch + sfa_base + off
-                    for h in range(8):
-                        dst = q * segb + 2 * pair_slot(8 * u + h, lpr, CPL)
-                        assert (dst + 2).max() <= nq * segb
-                        for b in range(2):
-                            dst_all.append(dst + b)
-                            src_all.append(src + 2 * h + b)
-            if direct:
                 it = np.arange(nq * nck)
                 q, c = it // nck, it % nck
                 r = np.minimum(slot_row(first, q), M - 1)
                 src = l * sfa_batch + r * nkb + 2 * (c0 + c)
                 assert src.min() >= 0 and (src + 2).max() <= L * sfa_batch
-                dst = q * segb + 2 * pair_slot(c, lpr, CPL)
-                assert (dst + 2).max() <= nq * segb
-                for b in range(2):
-                    dst_all.append(dst + b)
-                    src_all.append(src + b)
-            dst_cat = np.concatenate(dst_all)
-            assert np.unique(dst_cat).size == dst_cat.size, "two items write one LDS byte"
-            lds_src = np.full(nq * segb, -1, np.int64)
-            lds_src[np.concatenate(dst_all)] = np.concatenate(src_all)
+                assert (2 * it + 2).max() <= stb
+                lds_src[2 * it] = src
+                lds_src[2 * it + 1] = src + 1
             # ---- b': B chunk and its two SFB scales
             for k in range(CPL):
                 ci = c0 + np.minimum(j + k * lpr, nck - 1)
@@ -185,17 +156,25 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                 so = sf_offset(layout, np.zeros_like(ci), 2 * ci, nkb, ncb)
                 assert (so + 1).max() < sfb_batch
                 assert valid_sfb[so].all() and valid_sfb[so + 1].all()
-            # ---- compute side: lane j reads 2*CPL bytes at q*segb + j*2*CPL (any
-            # q < nq); every real (row, chunk) finds there the bytes staged from
-            # that row's two scales of that chunk
-            assert (np.arange(lpr) * 2 * CPL + 2 * CPL).max() <= segb
+
+            # ---- computing waves: lane j reads, for its chunk k and round row q,
+            # the 2 bytes at sfoff(c) + rowpart(q) (c, q clamped as in the kernel)
+            def staged_at(q, c):
+                if layout == 1:
+                    return (c >> 1) * nslots * 16 + (c & 1) * 2 + (q >> 2) * 16 + (q & 3) * 4
+                return (q * nck + c) * 2
+            for k in range(CPL):
+                cc = np.minimum(j + k * lpr, nck - 1)
+                for n in range(cdiv(nq, G) + 1):            # one round of read-ahead past the end
+                    q = np.minimum(grp + G * n, nq - 1)
+                    at = staged_at(q, cc)
+                    assert at.min() >= 0 and (at + 2).max() <= stb, "scale read outside the staging area"
             qs = np.arange(nq)[rows_all < M]
             if qs.size:
                 qq, cl, b = np.meshgrid(qs, np.arange(nck), np.arange(2), indexing="ij")
                 rq = rows_all[qq]
                 want = l * sfa_batch + sf_offset(layout, rq, 2 * (c0 + cl) + b, nkb, ncb)
-                jj, kk = cl % lpr, cl // lpr
-                got = lds_src[qq * segb + (jj * CPL + kk) * 2 + b]
+                got = lds_src[staged_at(qq, cl) + b]
                 assert np.array_equal(got, want), "staged scales do not match what the compute reads"
                 assert valid_sfa[want - l * sfa_batch].all()
         # ---- outputs

@@ -13,9 +13,17 @@
 // scale blocks, the scales of the four rows 128*(s/32) + 32*i4 + s%32,
 // i4 = 0..3. Each workgroup owns a contiguous range of slots of one batch,
 // i.e. 4 rows per slot, and one K-slice. With that row set the workgroup's
-// blocked scales are whole 16-byte vectors, read once, coalesced, into LDS;
-// plain scales are staged the same way, so both layouts run the same
-// arithmetic and give bit-identical results.
+// blocked scales are whole 16-byte vectors (neighbouring slots share lines),
+// read once into LDS; plain scales are staged from their rows. Both layouts
+// then run the same arithmetic and give bit-identical results.
+//
+// Roles. Four waves compute; a fifth stages the scales of the workgroup's
+// rows into LDS with direct-to-LDS loads (global_load_lds), all in flight at
+// once. A wave's vector loads complete in order, so scale loads issued by a
+// computing wave would hold back every later A load of that wave; from a wave
+// of their own they stream beside A. The computing waves start on A at once:
+// the first rounds keep their exact block sums and take the scales after the
+// barrier that publishes them.
 //
 // Inside a workgroup, LPR lanes share a row; lane j of a row group owns the
 // chunks j, j+LPR, j+2*LPR, j+3*LPR of every K-segment (4*LPR chunks), so each

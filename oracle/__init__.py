@@ -78,11 +78,11 @@ def _load():
     lib.nvo_fp16_to_double.restype = ctypes.c_double
     lib.nvo_fp16_to_double.argtypes = [ctypes.c_uint16]
     lib.nvo_gemv.restype = ctypes.c_int
-    lib.nvo_gemv.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
-                             vp, vp, vp, vp, vp]
+    lib.nvo_gemv.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                             ctypes.c_int, vp, vp, vp, vp, vp]
     lib.nvo_gemv_rows.restype = ctypes.c_int
-    lib.nvo_gemv_rows.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, ctypes.c_int, vp, i64,
-                                  ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.nvo_gemv_rows.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                  vp, i64, ctypes.c_int, vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -142,11 +142,12 @@ def fp16_bits_to_double(bits) -> np.ndarray:
 
 @dataclass
 class Result:
-    c: np.ndarray        # uint16 fp16 bits, [L][M] (or [n] for row subsets)
-    s_f64: np.ndarray    # plain fp64 sum
-    s_abs: np.ndarray    # fp64 sum of |a*sfa*b*sfb|
-    s_exact: np.ndarray  # exact sum in units of 2^-20 (int64)
+    c: np.ndarray        # uint16 fp16 bits of alpha * sum, [L][M] (or [n] for row subsets)
+    s_f64: np.ndarray    # plain fp64 sum, times alpha
+    s_abs: np.ndarray    # fp64 sum of |a*sfa*b*sfb|, times |alpha|
+    s_exact: np.ndarray  # exact unscaled sum in units of 2^-20 (int64)
     nan: np.ndarray      # 1 where a NaN scale was met
+    alpha: float = 1.0   # global float32 scale the call used
 
     @property
     def value(self) -> np.ndarray:
@@ -161,9 +162,21 @@ def _layout_id(layout) -> int:
     raise ValueError(layout)
 
 
-def gemv_arrays(a, b, sfa, sfb, M: int, K: int, L: int, layout, nthreads: int = 0) -> Result:
-    """Oracle GEMV on raw byte arrays (batch-outermost layouts, see synth)."""
+def _alpha32(alpha) -> float:
+    """alpha as the float32 the library takes (finite)."""
+    with np.errstate(over="ignore"):
+        a32 = np.float32(alpha)
+    if not np.isfinite(a32):
+        raise ValueError("alpha must be a finite float32")
+    return float(a32)
+
+
+def gemv_arrays(a, b, sfa, sfb, M: int, K: int, L: int, layout, nthreads: int = 0,
+                alpha: float = 1.0) -> Result:
+    """Oracle GEMV on raw byte arrays (batch-outermost layouts, see synth).
+    ``alpha`` is the global float32 scale: c = fp16(alpha * sum)."""
     lay = _layout_id(layout)
+    alpha = _alpha32(alpha)
     a, b, sfa, sfb = (np.ascontiguousarray(x, dtype=np.uint8) for x in (a, b, sfa, sfb))
     if a.size != L * M * K // 2 or b.size != L * K // 2:
         raise ValueError("A/B size mismatch")
@@ -176,25 +189,27 @@ def gemv_arrays(a, b, sfa, sfb, M: int, K: int, L: int, layout, nthreads: int = 
     se = np.zeros(n, np.int64)
     nan = np.zeros(n, np.uint8)
     nth = nthreads if nthreads > 0 else (os.cpu_count() or 1)
-    rc = _load().nvo_gemv(_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), M, K, L, lay, nth,
+    rc = _load().nvo_gemv(_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), M, K, L, lay, alpha, nth,
                           _ptr(c), _ptr(s), _ptr(sa), _ptr(se), _ptr(nan))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     shp = (L, M)
-    return Result(c.reshape(shp), s.reshape(shp), sa.reshape(shp), se.reshape(shp), nan.reshape(shp))
+    return Result(c.reshape(shp), s.reshape(shp), sa.reshape(shp), se.reshape(shp),
+                  nan.reshape(shp), alpha)
 
 
-def gemv(inp, layout="plain", nthreads: int = 0) -> Result:
+def gemv(inp, layout="plain", nthreads: int = 0, alpha: float = 1.0) -> Result:
     """Oracle GEMV of a ``synth.Inputs`` set, reading the scales in ``layout``."""
     w = inp.w
     return gemv_arrays(inp.a, inp.b, inp.sfa(layout), inp.sfb(layout), w.M, w.K, w.L,
-                       layout, nthreads)
+                       layout, nthreads, alpha)
 
 
-def gemv_rows(inp, rows, layout="plain", nthreads: int = 0) -> Result:
+def gemv_rows(inp, rows, layout="plain", nthreads: int = 0, alpha: float = 1.0) -> Result:
     """Oracle values of selected flattened rows (l*M + m) only."""
     w = inp.w
     lay = _layout_id(layout)
+    alpha = _alpha32(alpha)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     a, b = np.ascontiguousarray(inp.a), np.ascontiguousarray(inp.b)
     sfa, sfb = np.ascontiguousarray(inp.sfa(layout)), np.ascontiguousarray(inp.sfb(layout))
@@ -205,11 +220,11 @@ def gemv_rows(inp, rows, layout="plain", nthreads: int = 0) -> Result:
     se = np.zeros(n, np.int64)
     nan = np.zeros(n, np.uint8)
     nth = nthreads if nthreads > 0 else (os.cpu_count() or 1)
-    rc = _load().nvo_gemv_rows(_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), w.M, w.K, w.L, lay,
+    rc = _load().nvo_gemv_rows(_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), w.M, w.K, w.L, lay, alpha,
                                _ptr(rows), n, nth, _ptr(c), _ptr(s), _ptr(sa), _ptr(se), _ptr(nan))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
-    return Result(c, s, sa, se, nan)
+    return Result(c, s, sa, se, nan, alpha)
 
 
 # ---------------------------------------------------------------- tolerance
@@ -229,7 +244,7 @@ def check(gpu_bits, ref: Result, rel_tol: float = REL_TOL):
 
     Finite oracle value o: the GPU value g must be finite with
         |g - o| <= rel_tol * s_abs + ulp16(o).
-    Overflow edge: the GPU accumulates in fp32, so when the exact sum S is
+    Overflow edge: the GPU accumulates in fp32, so when the exact (scaled) sum S is
     within rel_tol * s_abs of 65520 (where float16 rounding switches between
     65504 and inf) either +-65504 or +-inf of the sign of S is accepted.
     Infinite oracle value: the GPU must give the same infinity (or the edge
@@ -239,7 +254,7 @@ def check(gpu_bits, ref: Result, rel_tol: float = REL_TOL):
     """
     g = fp16_bits_to_double(np.asarray(gpu_bits, dtype=np.uint16).reshape(ref.c.shape))
     o = fp16_bits_to_double(ref.c)
-    S = ref.s_exact.astype(np.float64) * 2.0 ** -20
+    S = ref.s_exact.astype(np.float64) * 2.0 ** -20 * ref.alpha
     tol = rel_tol * ref.s_abs + ulp16(np.where(np.isfinite(o), o, 0.0))
     ok = np.zeros(o.shape, dtype=bool)
 
@@ -271,5 +286,5 @@ def check_report(gpu_bits, ref: Result, rel_tol: float = REL_TOL, max_show: int 
     for idx in bad[:max_show]:
         idx = tuple(idx)
         lines.append(f"  at {idx}: gpu={g[idx]!r} oracle={o[idx]!r} "
-                     f"S={ref.s_exact[idx] * 2.0 ** -20!r} s_abs={ref.s_abs[idx]!r}")
+                     f"S={ref.s_exact[idx] * 2.0 ** -20 * ref.alpha!r} s_abs={ref.s_abs[idx]!r}")
     return "\n".join(lines)

@@ -22,6 +22,13 @@
  * Alongside it keeps a plain fp64 sum and the fp64 sum of |products|, which
  * the parity tolerance uses.
  *
+ * Optional global scale (the per-tensor float32 scale of NVFP4's two-level
+ * scaling, mentioned in submission 69575's description of the format and
+ * applied nowhere on the pages): c = fp16(alpha * sum). alpha is a finite
+ * float32, alpha = ma * 2^ea with a 24-bit integer ma, so alpha * sum is the
+ * exact integer |sum| * ma (below 2^87, formed in 128 bits) times a power of
+ * two, rounded once. alpha = 1 gives the plain result.
+ *
  * Operand formats (the `cute_kernel` module constants name them:
  * Float4E2M1FN elements, Float8E4M3FN scales, 16 elements per scale):
  *   E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; no inf or NaN.
@@ -233,7 +240,36 @@ typedef struct {
     const uint8_t *a, *b, *sfa, *sfb;
     int64_t M, K, L;
     int layout;
+    float alpha;
 } problem_t;
+
+/* fp16 of alpha * (sum in 2^-20 units), exactly rounded (see the header). */
+static uint16_t round_scaled(int64_t exact, float alpha)
+{
+    int ea;
+    const float fa = frexpf(fabsf(alpha), &ea);         /* |alpha| = fa * 2^ea, fa in [0.5, 1) */
+    const uint64_t ma = (uint64_t)ldexpf(fa, 24);       /* exact 24-bit integer */
+    const int neg = (exact < 0) != (signbit(alpha) != 0);
+    const uint64_t mag_s = exact < 0 ? (uint64_t)(-exact) : (uint64_t)exact;
+    unsigned __int128 prod = (unsigned __int128)mag_s * ma;
+    int e2 = -20 + ea - 24;
+    int sh = 0;
+    uint64_t mag;
+    if (alpha == 0.0f || mag_s == 0)
+        return neg ? 0x8000u : 0u;
+    /* keep 62 significant bits and a sticky bit: rounding to 11 bits below
+       them is unchanged */
+    while ((prod >> (62 + sh)) != 0)
+        ++sh;
+    if (sh > 0) {
+        const unsigned __int128 lost = prod & ((((unsigned __int128)1) << sh) - 1);
+        mag = (uint64_t)(prod >> sh) | (lost != 0 ? 1u : 0u);
+    } else {
+        mag = (uint64_t)prod;
+    }
+    e2 += sh;
+    return nvo_fp16_round(neg, mag, e2);
+}
 
 typedef struct {
     uint16_t c;
@@ -274,10 +310,9 @@ static row_result_t gemv_row(const problem_t *pb, int64_t row)
         sabs += fabs(t);
         exact += g_e2m1_q[ac] * g_e4m3_q[sa] * g_e2m1_q[bc] * g_e4m3_q[sb];
     }
-    r.c = nan ? (uint16_t)0x7E00u
-              : nvo_fp16_round(exact < 0, exact < 0 ? (uint64_t)(-exact) : (uint64_t)exact, -20);
-    r.s_f64 = nan ? NAN : s;
-    r.s_abs = sabs;
+    r.c = nan ? (uint16_t)0x7E00u : round_scaled(exact, pb->alpha);
+    r.s_f64 = nan ? NAN : s * (double)pb->alpha;
+    r.s_abs = sabs * fabs((double)pb->alpha);
     r.s_exact = exact;
     r.nan = (uint8_t)nan;
     return r;
@@ -341,46 +376,47 @@ static int run_jobs(const problem_t *pb, const int64_t *rows, int64_t nout, int 
 }
 
 static int valid(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const uint8_t *sfb,
-                 int64_t M, int64_t K, int64_t L, int layout, const uint16_t *c)
+                 int64_t M, int64_t K, int64_t L, int layout, float alpha, const uint16_t *c)
 {
     return M >= 1 && L >= 1 && K >= 32 && K % 32 == 0 && K <= (INT64_C(1) << 20) &&
-           (layout == 0 || layout == 1) && a && b && sfa && sfb && c;
+           (layout == 0 || layout == 1) && isfinite(alpha) && a && b && sfa && sfb && c;
 }
 
 /*
  * Full batched GEMV. Rows (l, m) are split over `nthreads` threads; each row
  * is summed in increasing k, so the result does not depend on the thread
  * count. c, s_f64, s_abs, s_exact and nan_flag hold L*M entries at index
- * l*M + m; all but c may be NULL. s_exact is the exact sum in units of 2^-20.
+ * l*M + m; all but c may be NULL. s_exact is the exact unscaled sum in units
+ * of 2^-20; c, s_f64 and s_abs include the global scale alpha.
  * Returns 0, or -1 for invalid arguments.
  */
 int nvo_gemv(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const uint8_t *sfb,
-             int64_t M, int64_t K, int64_t L, int layout, int nthreads,
+             int64_t M, int64_t K, int64_t L, int layout, float alpha, int nthreads,
              uint16_t *c, double *s_f64, double *s_abs, int64_t *s_exact, uint8_t *nan_flag)
 {
     problem_t pb;
-    if (!valid(a, b, sfa, sfb, M, K, L, layout, c))
+    if (!valid(a, b, sfa, sfb, M, K, L, layout, alpha, c))
         return -1;
     pthread_once(&g_once, init_tables);
     pb.a = a; pb.b = b; pb.sfa = sfa; pb.sfb = sfb;
-    pb.M = M; pb.K = K; pb.L = L; pb.layout = layout;
+    pb.M = M; pb.K = K; pb.L = L; pb.layout = layout; pb.alpha = alpha;
     return run_jobs(&pb, NULL, M * L, nthreads, c, s_f64, s_abs, s_exact, nan_flag);
 }
 
 /* Selected rows only (spot checks at full size): rows[i] = l*M + m, output slot i. */
 int nvo_gemv_rows(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const uint8_t *sfb,
-                  int64_t M, int64_t K, int64_t L, int layout, const int64_t *rows, int64_t nrows,
-                  int nthreads, uint16_t *c, double *s_f64, double *s_abs, int64_t *s_exact,
-                  uint8_t *nan_flag)
+                  int64_t M, int64_t K, int64_t L, int layout, float alpha, const int64_t *rows,
+                  int64_t nrows, int nthreads, uint16_t *c, double *s_f64, double *s_abs,
+                  int64_t *s_exact, uint8_t *nan_flag)
 {
     problem_t pb;
-    if (!valid(a, b, sfa, sfb, M, K, L, layout, c) || !rows)
+    if (!valid(a, b, sfa, sfb, M, K, L, layout, alpha, c) || !rows)
         return -1;
     for (int64_t i = 0; i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= M * L)
             return -1;
     pthread_once(&g_once, init_tables);
     pb.a = a; pb.b = b; pb.sfa = sfa; pb.sfb = sfb;
-    pb.M = M; pb.K = K; pb.L = L; pb.layout = layout;
+    pb.M = M; pb.K = K; pb.L = L; pb.layout = layout; pb.alpha = alpha;
     return run_jobs(&pb, rows, nrows, nthreads, c, s_f64, s_abs, s_exact, nan_flag);
 }

@@ -5,6 +5,7 @@ names mirror the C ABI in include/nvfp4_gemv.h. torch provides device memory and
 the stream; tensors are passed as raw device pointers.
 
     nvfp4_gemv(a, b, sfa, sfb, c, M, K, L, sf_layout, stream=None)
+    nvfp4_gemv_scaled(..., sf_layout, alpha, workspace=None, stream=None)
 
     a   uint8 [L, M, K/2]   packed E2M1, low nibble = even k
     b   uint8 [L, K/2]
@@ -31,11 +32,13 @@ NVFP4_ERR_MISALIGNED = 3
 NVFP4_ERR_INVALID_LAYOUT = 4
 NVFP4_ERR_WORKSPACE = 5
 NVFP4_ERR_HIP = 6
+NVFP4_ERR_INVALID_SCALE = 7
 
 EXPORTED_SYMBOLS = (
     "nvfp4_gemv",
     "nvfp4_gemv_workspace_bytes",
     "nvfp4_gemv_ex",
+    "nvfp4_gemv_scaled",
     "nvfp4_gemv_plan",
     "nvfp4_status_string",
     "nvfp4_last_hip_error",
@@ -81,6 +84,9 @@ def lib():
     L.nvfp4_gemv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.nvfp4_gemv_ex.restype = i32
     L.nvfp4_gemv_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
+    L.nvfp4_gemv_scaled.restype = i32
+    L.nvfp4_gemv_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_float, vp,
+                                    ctypes.c_size_t, vp]
     L.nvfp4_gemv_workspace_bytes.restype = ctypes.c_size_t
     L.nvfp4_gemv_workspace_bytes.argtypes = [i64, i64, i64]
     L.nvfp4_gemv_plan.restype = i32
@@ -179,6 +185,22 @@ def nvfp4_gemv_ex(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, workspac
                              _stream_handle(stream))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemv_ex")
+
+
+def nvfp4_gemv_scaled(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, alpha: float,
+                      workspace=None, workspace_bytes: int | None = None, stream=None) -> None:
+    """Enqueue c = fp16(alpha * GEMV(a, b, sfa, sfb)); ``workspace`` None uses
+    the library-owned one, else a caller-owned (zero-initialised) workspace."""
+    (pa, na), (pb, nb), (psa, nsa), (psb, nsb), (pc, nc) = map(_ptr_and_bytes, (a, b, sfa, sfb, c))
+    pw, nw = _ptr_and_bytes(workspace)
+    if workspace_bytes is None:
+        workspace_bytes = nw or 0
+    lay = layout_id(sf_layout)
+    _check_sizes(M, K, L, lay, a=na, b=nb, sfa=nsa, sfb=nsb, c=nc)
+    st = lib().nvfp4_gemv_scaled(pa, pb, psa, psb, pc, M, K, L, lay, float(alpha), pw,
+                                 workspace_bytes, _stream_handle(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemv_scaled")
 
 
 def nvfp4_gemv_plan(M: int, K: int, L: int) -> dict:

@@ -39,8 +39,10 @@
 // Rows follow each other without a break: the loads of the next kPrefetch
 // chunk-steps are always in flight. A row's lanes are summed with DPP and the
 // per-wave sums are added in LDS in a fixed order; the result is rounded to
-// float16 once. K-split shapes (small M*L) write float32 partials and the last
-// workgroup of a row range (atomic ticket) adds them in slice order.
+// float16 once, after one float32 multiply by the global scale alpha (1 for
+// the unscaled entry points, where it changes nothing). K-split shapes (small
+// M*L) write float32 partials and the last workgroup of a row range (atomic
+// ticket) adds them in slice order.
 //
 // Workgroup ids are remapped so that each XCD (own L2) gets a contiguous range
 // of slots; the batch index is part of the grid, so one launch covers all L.
@@ -48,6 +50,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -94,6 +97,7 @@ struct Params {
     int64_t sfa_batch;    // bytes per batch of SFA
     int64_t sfb_batch;    // bytes per batch of SFB
     int64_t a_bytes;      // bytes of A (all batches)
+    float alpha;          // global scale, applied to the float32 row sum before rounding
     uint32_t *counters;   // tickets [L][P] when S > 1
     float *partials;      // [L*M][S] when S > 1
 };
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
 #pragma unroll
                 for (int w = 1; w < WPG; ++w)
                     v += part[q * WPG + w];
-                C[abatch + r] = f16_bits(v);
+                C[abatch + r] = f16_bits(v * p.alpha);
             }
         }
         return;
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
             float v = 0.0f;
             for (int k = 0; k < p.S; ++k)
                 v += __hip_atomic_load(pp + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            C[abatch + r] = f16_bits(v);
+            C[abatch + r] = f16_bits(v * p.alpha);
         }
     }
 }
@@ -708,10 +712,11 @@ nvfp4_status_t validate(const void *a, const void *b, const void *sfa, const voi
 }
 
 nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void *sfb, void *c,
-                      int64_t M, int64_t K, int64_t L, int sf_layout, const Plan &pl,
+                      int64_t M, int64_t K, int64_t L, int sf_layout, float alpha, const Plan &pl,
                       void *ws, hipStream_t st)
 {
     Params p{};
+    p.alpha = alpha;
     p.M = (int32_t)M;
     p.K = (int32_t)K;
     p.L = (int32_t)L;
@@ -807,7 +812,7 @@ nvfp4_status_t nvfp4_gemv(const void *a, const void *b, const void *sfa, const v
     void *ws = nullptr;
     if (pl.ws_total > 0 && (st = device_workspace(pl.ws_total, &ws)) != NVFP4_OK)
         return st;
-    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, pl, ws, (hipStream_t)stream);
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, ws, (hipStream_t)stream);
 }
 
 size_t nvfp4_gemv_workspace_bytes(int64_t M, int64_t K, int64_t L)
@@ -828,7 +833,32 @@ nvfp4_status_t nvfp4_gemv_ex(const void *a, const void *b, const void *sfa, cons
     if (pl.ws_total > 0 &&
         (!workspace || workspace_bytes < pl.ws_total || !aligned(workspace, kWsAlign)))
         return NVFP4_ERR_WORKSPACE;
-    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, pl, workspace, (hipStream_t)stream);
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, workspace, (hipStream_t)stream);
+}
+
+nvfp4_status_t nvfp4_gemv_scaled(const void *a, const void *b, const void *sfa, const void *sfb,
+                                 void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
+                                 float alpha, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    nvfp4_status_t st = validate(a, b, sfa, sfb, c, M, K, L, sf_layout);
+    if (st != NVFP4_OK)
+        return st;
+    if (!std::isfinite(alpha))
+        return NVFP4_ERR_INVALID_SCALE;
+    const Plan pl = make_plan(M, K, L);
+    void *ws = workspace;
+    if (pl.ws_total > 0) {
+        if (!workspace) {
+            if (workspace_bytes != 0)
+                return NVFP4_ERR_WORKSPACE;
+            if ((st = device_workspace(pl.ws_total, &ws)) != NVFP4_OK)
+                return st;
+        } else if (workspace_bytes < pl.ws_total || !aligned(workspace, kWsAlign)) {
+            return NVFP4_ERR_WORKSPACE;
+        }
+    }
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, pl, ws, (hipStream_t)stream);
 }
 
 nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan)
@@ -859,6 +889,7 @@ const char *nvfp4_status_string(int status)
     case NVFP4_ERR_INVALID_LAYOUT: return "invalid scale layout";
     case NVFP4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case NVFP4_ERR_HIP: return "HIP runtime error";
+    case NVFP4_ERR_INVALID_SCALE: return "global scale alpha is not finite";
     default: return "unknown status";
     }
 }

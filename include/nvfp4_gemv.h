@@ -67,7 +67,8 @@ typedef enum {
     NVFP4_ERR_MISALIGNED = 3,       /* a pointer misses its required alignment     */
     NVFP4_ERR_INVALID_LAYOUT = 4,   /* sf_layout is not an nvfp4_sf_layout_t       */
     NVFP4_ERR_WORKSPACE = 5,        /* workspace missing, misaligned or too small  */
-    NVFP4_ERR_HIP = 6               /* a HIP call failed; see nvfp4_last_hip_error */
+    NVFP4_ERR_HIP = 6,              /* a HIP call failed; see nvfp4_last_hip_error */
+    NVFP4_ERR_INVALID_SCALE = 7     /* the global scale alpha is NaN or infinite   */
 } nvfp4_status_t;
 
 /*
@@ -99,6 +100,31 @@ size_t nvfp4_gemv_workspace_bytes(int64_t M, int64_t K, int64_t L);
 nvfp4_status_t nvfp4_gemv_ex(const void *a, const void *b, const void *sfa, const void *sfb,
                              void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Batched GEMV with NVFP4's second scaling level: one float32 scale per tensor
+ * pair on top of the per-16-element E4M3 scales (the "dual scaling" that
+ * kernelbot NVFP4 GEMV submission 69575 lists among its notes on the format;
+ * none of the pages' kernels applies it, so its placement is this library's
+ * reading: it multiplies the finished float32 row sum once, before the cast):
+ *
+ *   c[l][m] = fp16( alpha * sum_{k<K} e2m1(A) * e4m3(SFA) * e2m1(B) * e4m3(SFB) )
+ *
+ * A caller whose A and B carry global scales ga and gb passes alpha = ga * gb.
+ * alpha must be finite (else NVFP4_ERR_INVALID_SCALE, nothing launched); with
+ * alpha = 1 the result is bit-identical to nvfp4_gemv. The product alpha * sum
+ * is rounded to float32 and then to float16 (two roundings, within the
+ * library's float32-accumulation error). Layouts, alignment and the other
+ * arguments are as for nvfp4_gemv.
+ * Workspace: NULL with workspace_bytes = 0 uses the library-owned workspace as
+ * nvfp4_gemv does; otherwise it is a caller-owned workspace with the
+ * requirements of nvfp4_gemv_ex (NVFP4_ERR_WORKSPACE if too small or
+ * misaligned when the shape needs one).
+ */
+nvfp4_status_t nvfp4_gemv_scaled(const void *a, const void *b, const void *sfa, const void *sfb,
+                                 void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
+                                 float alpha, void *workspace, size_t workspace_bytes,
+                                 void *stream);
 
 /*
  * Launch plan chosen for a shape (for tests and reports). Returns NVFP4_OK and

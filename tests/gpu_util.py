@@ -24,14 +24,18 @@ class DeviceInputs:
         self.sfb = {"plain": to_dev(inp.sfb_plain), "blocked": to_dev(inp.sfb_blocked)}
 
 
-def run(dev: DeviceInputs, layout: str, workspace=None, stream=None) -> np.ndarray:
-    """One GEMV call; returns the float16 bits [L][M]. Checks the canary tail."""
+def run(dev: DeviceInputs, layout: str, workspace=None, stream=None, alpha=None) -> np.ndarray:
+    """One GEMV call; returns the float16 bits [L][M]. Checks the canary tail.
+    With ``alpha`` the call goes through nvfp4_gemv_scaled."""
     w = dev.inp.w
     n = w.L * w.M
     c = torch.empty(n + CANARY_TAIL, dtype=torch.float16, device="cuda")
     c.view(torch.int16).fill_(-1)          # 0xFFFF everywhere: unwritten outputs stay NaN
     c_out = c[:n]
-    if workspace is None:
+    if alpha is not None:
+        g.nvfp4_gemv_scaled(dev.a, dev.b, dev.sfa[layout], dev.sfb[layout], c_out, w.M, w.K, w.L,
+                            layout, alpha, workspace, stream=stream)
+    elif workspace is None:
         g.nvfp4_gemv(dev.a, dev.b, dev.sfa[layout], dev.sfb[layout], c_out, w.M, w.K, w.L,
                      layout, stream)
     else:

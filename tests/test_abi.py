@@ -85,6 +85,34 @@ def test_ex_workspace_errors():
     assert lib.nvfp4_gemv_ex(*base[:5], M, 33, L, 1, None, 0, None) == g.NVFP4_ERR_INVALID_SHAPE
 
 
+def scaled(alpha=1.0, ws=None, ws_bytes=0, M=128, K=256, L=1, **kw):
+    args = dict(OK_ARGS)
+    args.update(kw)
+    return g.lib().nvfp4_gemv_scaled(args["a"], args["b"], args["sfa"], args["sfb"], args["c"],
+                                     M, K, L, 1, alpha, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("alpha", [float("nan"), float("inf"), float("-inf")])
+def test_scaled_rejects_non_finite_alpha(alpha):
+    assert scaled(alpha) == g.NVFP4_ERR_INVALID_SCALE
+
+
+def test_scaled_validation_order():
+    # pointer, shape and alignment errors come before the scale check
+    assert scaled(float("nan"), a=None) == g.NVFP4_ERR_NULL_POINTER
+    assert scaled(float("nan"), K=48) == g.NVFP4_ERR_INVALID_SHAPE
+    assert scaled(float("nan"), c=OK_ARGS["c"] + 1) == g.NVFP4_ERR_MISALIGNED
+
+
+def test_scaled_workspace_errors():
+    M, K, L = 127, 16384, 1
+    need = g.lib().nvfp4_gemv_workspace_bytes(M, K, L)
+    assert need > 0
+    assert scaled(0.5, None, need, M, K, L) == g.NVFP4_ERR_WORKSPACE       # NULL with a size
+    assert scaled(0.5, 0x200000, need - 1, M, K, L) == g.NVFP4_ERR_WORKSPACE
+    assert scaled(0.5, 0x200010, need, M, K, L) == g.NVFP4_ERR_WORKSPACE
+
+
 def test_workspace_bytes():
     lib = g.lib()
     for w in (synth.BALANCED, synth.BATCHED, synth.HEADLINE, synth.TINY):
@@ -134,7 +162,7 @@ def test_plan_rejects_bad_shape():
 
 
 def test_status_strings():
-    for st in range(0, 7):
+    for st in range(0, 8):
         assert g.status_string(st)
     assert g.status_string(1234) == "unknown status"
 

@@ -235,10 +235,10 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t s = (int32_t)(lid % (uint32_t)p.S);
-    const uint32_t t2 = lid / (uint32_t)p.S;
-    const int32_t tile = (int32_t)(t2 % (uint32_t)p.P);
-    const int32_t l = (int32_t)(t2 / (uint32_t)p.P);
+    const int32_t s = SPLIT ? (int32_t)(lid % (uint32_t)p.S) : 0;
+    const uint32_t t2 = SPLIT ? lid / (uint32_t)p.S : lid;
+    const int32_t tile = p.L == 1 ? (int32_t)t2 : (int32_t)(t2 % (uint32_t)p.P);
+    const int32_t l = p.L == 1 ? 0 : (int32_t)(t2 / (uint32_t)p.P);
 
     const int32_t M = p.M, K = p.K;
     const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
@@ -290,31 +290,47 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     // the first) and one that publishes the staged scales; then the ones of
     // the epilogue.
     if (loader) {
+        // raised issue priority: its copies gate the publish barrier, and the
+        // computing waves' A loads would otherwise take every free issue slot
+        __builtin_amdgcn_s_setprio(3);
         for (int32_t c0 = c_begin; c0 < c_end; c0 += SEG) {
             const int32_t nck = min(SEG, c_end - c0);
             if (c0 != c_begin)
                 __syncthreads();                           // the previous segment's scales are read
             const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1, units = nck >> 3;
             if (!direct) {
-                // wave-wide direct-to-LDS load i puts item i*64 + lane at
-                // (i*64 + lane) * 16 (lanes past the items repeat the last
-                // item, inside the area); all loads are in flight at once
-                const int32_t items = LAYOUT == NVFP4_SF_BLOCKED ? nslots * ncb_seg : nq * units;
-                const int32_t nload = (items + 63) >> 6;
+                // Wave-wide direct-to-LDS load i puts item i*64 + lane at
+                // (i*64 + lane) * 16; all loads are in flight at once. Item it
+                // is (minor, major) = (it % per, it / per) with per = nslots
+                // (blocked: slot, 4-block group) or units (plain: 16-byte
+                // unit, row). The lane steps its pair by 64 items per load
+                // without dividing: issuing must be quick, or the scales land
+                // late. Items past the end clamp the major index (in bounds;
+                // those LDS bytes are never read).
+                const int32_t per = LAYOUT == NVFP4_SF_BLOCKED ? nslots : units;
+                const int32_t nmajor = LAYOUT == NVFP4_SF_BLOCKED ? ncb_seg : nq;
+                const int32_t nload = (per * nmajor + 63) >> 6;
+                const int32_t dmaj = 64 / per, dmin = 64 % per;
+                int32_t mn = lane % per, mj = lane / per;
                 for (int32_t i = 0; i < nload; ++i) {
-                    const int32_t it = min(i * 64 + lane, items - 1);
+                    const int32_t mjc = min(mj, nmajor - 1);
                     const uint8_t *src;
                     if (LAYOUT == NVFP4_SF_BLOCKED) {
-                        const int32_t sg = first + it % nslots, cb = it / nslots;
-                        src = sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16;
+                        const int32_t sg = first + mn;
+                        src = sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + mjc) * 512 + (sg & 31) * 16;
                     } else {
-                        const int32_t q = it / units, u = it % units;
-                        const int32_t r = min(slot_row(first, q), M - 1);
-                        src = sfa_l + (int64_t)r * nkb + 2 * c0 + 16 * u;
+                        const int32_t r = min(slot_row(first, mjc), M - 1);
+                        src = sfa_l + (int64_t)r * nkb + 2 * c0 + 16 * mn;
                     }
                     __builtin_amdgcn_global_load_lds((const void *)src,
                                                      (__attribute__((address_space(3))) void *)(stage + i * kDmaBytes),
                                                      16, 0, 0);
+                    mn += dmin;
+                    mj += dmaj;
+                    if (mn >= per) {
+                        mn -= per;
+                        ++mj;
+                    }
                 }
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the staged bytes are in LDS
             } else {
@@ -429,7 +445,12 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 store_row(grp + G * n, acc);
         };
 
-        // ---- B and SFB for b', then the first kPrefetch steps of A
+        // ---- the first kPrefetch steps of A, then B and SFB for b' (A first:
+        // b' waits for all of them anyway, and the stream starts sooner)
+#pragma unroll
+        for (int u = 0; u < kPrefetch; ++u)
+            abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
+        __builtin_amdgcn_sched_barrier(0);
         uint4_t bload[kCpl];
         uint32_t sload[kCpl];
 #pragma unroll
@@ -438,10 +459,6 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
             bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
             sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < kPrefetch; ++u)
-            abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
         __builtin_amdgcn_sched_barrier(0);
         // b' for this lane's chunks of the segment (registers, reused for every row)
 #pragma unroll

@@ -121,12 +121,12 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                 nload = cdiv(items, 64)
                 dst_all, src_all = [], []
                 for i in range(nload):
-                    it = np.minimum(i * 64 + lane, items - 1)
+                    it = i * 64 + lane              # past the end: the major index is clamped
                     if layout == 1:
-                        sg, cb = first + it % nslots, it // nslots
+                        sg, cb = first + it % nslots, np.minimum(it // nslots, ncb_seg - 1)
                         src = ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
                     else:
-                        q, u = it // units, it % units
+                        q, u = np.minimum(it // units, nq - 1), it % units
                         r = np.minimum(slot_row(first, q), M - 1)
                         assert (2 * c0 + 16 * u + 16).max() <= nkb
                         src = r * nkb + 2 * c0 + 16 * u

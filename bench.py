@@ -105,6 +105,73 @@ def cpu_baseline(w, layout: str, budget_s: float):
             "us_per_call": round(sec_per_call * 1e6, 1)}
 
 
+def bench_reblock(args, w, dev):
+    """Device reblock of the workload's plain SFA [L][M][K/16] into the 128x4
+    blocked layout: HBM bytes = plain read + blocked write."""
+    import torch
+    import block_scaled_fp4_gemv_amd as g
+    M, K, L = w.M, w.K, w.L
+    in_bytes = L * M * (K // 16)
+    out_bytes = g.nvfp4_blocked_scales_bytes(M, K, L)
+    nsets = max(1, min(64, -(-ROTATE_BYTES // (in_bytes + out_bytes))))
+    log(f"reblock {w.name}: {nsets} sets of {in_bytes / 1e6:.2f} MB plain -> {out_bytes / 1e6:.2f} MB blocked")
+    plains, outs = [], []
+    for i in range(nsets):
+        plains.append(torch.from_numpy(synth.make_inputs(w, i).sfa_plain).to(dev))
+        outs.append(torch.empty(out_bytes, dtype=torch.uint8, device=dev))
+    for i in range(args.warmup):
+        g.nvfp4_scales_to_blocked(plains[i % nsets], outs[i % nsets], M, K, L)
+    torch.cuda.synchronize()
+    verified = None
+    if not args.no_verify:
+        import oracle
+        oracle.build(force=False)
+        g.nvfp4_scales_to_blocked(plains[0], outs[0], M, K, L)
+        torch.cuda.synchronize()
+        want = oracle.reblock(plains[0].cpu().numpy(), M, K, L).reshape(-1)
+        verified = bool(np.array_equal(outs[0].cpu().numpy(), want))
+        log(f"reblock parity vs oracle: {'ok' if verified else 'FAILED'}")
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(args.steps):
+            g.nvfp4_scales_to_blocked(plains[i % nsets], outs[i % nsets], M, K, L, cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
+    out = {"metric": "µs/call and achieved HBM GB/s of the plain -> 128x4 blocked SFA reblock",
+           "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": f"reblock_sfa_{w.name}", "rows": M, "K": K, "L": L,
+                      "plain_bytes": in_bytes, "blocked_bytes": out_bytes, "rotating_sets": nsets},
+           "us_per_call": round(ms * 1e3, 3), "verified_vs_oracle": verified,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        p0 = plains[0].cpu().numpy()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.reblock(p0, M, K, L)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_budget, 5.0) or reps >= 50:
+                break
+        out["cpu_baseline"] = {"value": round((in_bytes + out_bytes) / (el / reps) / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} full reblocks of input set 0", "us_per_call": round(el / reps * 1e6, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +182,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--reblock", action="store_true",
+                    help="time the device plain -> blocked reblock of the workload's SFA instead "
+                         "(its own JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run torch's device copy of BYTES bytes --steps times (a plain copy "
                          "kernel of known size, to scale hardware byte counters)")
@@ -144,6 +214,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = WORKLOADS[args.workload]
+    if args.reblock:
+        bench_reblock(args, w, dev)
+        return
     layout = args.layout
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")

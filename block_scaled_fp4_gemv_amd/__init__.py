@@ -6,6 +6,7 @@ the stream; tensors are passed as raw device pointers.
 
     nvfp4_gemv(a, b, sfa, sfb, c, M, K, L, sf_layout, stream=None)
     nvfp4_gemv_scaled(..., sf_layout, alpha, workspace=None, stream=None)
+    nvfp4_scales_to_blocked(plain, blocked, rows, K, L, stream=None)
 
     a   uint8 [L, M, K/2]   packed E2M1, low nibble = even k
     b   uint8 [L, K/2]
@@ -40,6 +41,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_gemv_ex",
     "nvfp4_gemv_scaled",
     "nvfp4_gemv_plan",
+    "nvfp4_scales_to_blocked",
+    "nvfp4_blocked_scales_bytes",
     "nvfp4_status_string",
     "nvfp4_last_hip_error",
 )
@@ -91,6 +94,10 @@ def lib():
     L.nvfp4_gemv_workspace_bytes.argtypes = [i64, i64, i64]
     L.nvfp4_gemv_plan.restype = i32
     L.nvfp4_gemv_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    L.nvfp4_scales_to_blocked.restype = i32
+    L.nvfp4_scales_to_blocked.argtypes = [vp, vp, i64, i64, i64, vp]
+    L.nvfp4_blocked_scales_bytes.restype = ctypes.c_size_t
+    L.nvfp4_blocked_scales_bytes.argtypes = [i64, i64, i64]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_last_hip_error.restype = i32
@@ -209,6 +216,24 @@ def nvfp4_gemv_plan(M: int, K: int, L: int) -> dict:
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemv_plan")
     return plan.as_dict()
+
+
+def nvfp4_blocked_scales_bytes(rows: int, K: int, L: int) -> int:
+    return int(lib().nvfp4_blocked_scales_bytes(rows, K, L))
+
+
+def nvfp4_scales_to_blocked(plain, blocked, rows: int, K: int, L: int, stream=None) -> None:
+    """Enqueue the plain -> 128x4 blocked reblock of a scale tensor.
+    plain uint8 [L, rows, K/16]; blocked uint8 of nvfp4_blocked_scales_bytes bytes."""
+    (pp, npb), (pb, nbb) = _ptr_and_bytes(plain), _ptr_and_bytes(blocked)
+    need = nvfp4_blocked_scales_bytes(rows, K, L)
+    if need and npb is not None and npb < L * rows * (K // 16):
+        raise ValueError(f"plain holds {npb} bytes, the shape needs {L * rows * (K // 16)}")
+    if need and nbb is not None and nbb < need:
+        raise ValueError(f"blocked holds {nbb} bytes, the shape needs {need}")
+    st = lib().nvfp4_scales_to_blocked(pp, pb, rows, K, L, _stream_handle(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_scales_to_blocked")
 
 
 def nvfp4_status_string(status: int) -> str:

@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "nvfp4_gemv.hip")
+SRCS = [os.path.join(PKG, "csrc", "nvfp4_gemv.hip"), os.path.join(PKG, "csrc", "nvfp4_reblock.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4gemv.so")
 
@@ -35,9 +35,9 @@ def hipcc() -> str:
 
 
 def build(extra_flags=None, out: str = LIB, verbose: bool = False) -> str:
-    """Compile csrc/nvfp4_gemv.hip into ``out``. Always recompiles."""
+    """Compile the HIP sources in csrc/ into ``out``. Always recompiles."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -58,6 +58,7 @@
 #include <vector>
 
 #include "nvfp4_gemv.h"
+#include "nvfp4_internal.h"
 
 namespace {
 
@@ -914,3 +915,5 @@ const char *nvfp4_status_string(int status)
 int nvfp4_last_hip_error(void) { return g_last_hip_error; }
 
 } // extern "C"
+
+void nvfp4_record_hip_error(int error) { g_last_hip_error = error; }

@@ -1,0 +1,146 @@
+// Plain -> 128x4 blocked reblocking of NVFP4 scale factors on MI355X (gfx950).
+//
+// The blocked ("permuted") layout is the one kernelbot NVFP4 GEMV submission
+// 69953 builds with `to_blocked_batch` and submission 69575 with
+// `blocked_transform_kernel`: a rows x cols matrix of E4M3 codes (cols = K/16)
+// is cut into 128x4 tiles, tile (rb, cb) is stored as 512 contiguous bytes at
+// (rb * ceil(cols/4) + cb) * 512, and inside a tile scale (r, c) sits at
+// (r % 32) * 16 + (r / 32) * 4 + c. So each 16-byte line of a tile holds the
+// 4 scales of rows r, r+32, r+64, r+96. Padding (rows >= rows, columns >=
+// cols) is written as zero bytes.
+//
+// Work split. A workgroup of 256 threads owns one batch, one 128-row block
+// and kTilesPerWg consecutive tiles of it. It reads the 128 rows x 4*kTilesPerWg
+// plain bytes row by row (consecutive threads take consecutive words of a row,
+// so the reads are contiguous runs), parks them in LDS, and writes the tiles
+// as contiguous 16-byte lines (consecutive threads write consecutive lines).
+// The kernel is a byte shuffle: it is bound by HBM, with read bytes = the
+// plain scales and write bytes = the blocked scales (padding included).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "nvfp4_gemv.h"
+#include "nvfp4_internal.h"
+
+namespace {
+
+typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRbThreads = 256;
+constexpr int kTilesPerWg = 16;                 // 64 scale columns per workgroup
+constexpr int kWordsPerRow = kTilesPerWg;       // one 4-byte word per tile and row
+constexpr int kLdsPitch = kWordsPerRow + 1;     // words; odd pitch avoids bank conflicts
+
+struct ReblockParams {
+    int32_t rows, cols;                         // plain matrix per batch (cols = K/16)
+    int32_t nrb, ncb;                           // 128-row blocks, 4-column groups
+    int32_t wg_per_rb;                          // workgroups per row block
+    int64_t in_batch, out_batch;                // bytes per batch
+};
+
+// 4 plain bytes of row r, columns 4*cb .. 4*cb+3 (zero past the matrix),
+// little-endian in a word. WORDS: the row starts are 4-byte aligned.
+template <bool WORDS>
+__device__ inline uint32_t load_word(const uint8_t *__restrict__ in, const ReblockParams &p, int32_t r, int32_t cb)
+{
+    if (r >= p.rows || 4 * cb >= p.cols)
+        return 0u;
+    const uint8_t *src = in + (int64_t)r * p.cols + 4 * cb;
+    if (WORDS && 4 * cb + 4 <= p.cols)
+        return *(const uint32_t *)src;
+    uint32_t w = 0;
+    const int32_t n = min(4, p.cols - 4 * cb);
+    for (int32_t i = 0; i < n; ++i)
+        w |= (uint32_t)src[i] << (8 * i);
+    return w;
+}
+
+template <bool WORDS>
+__global__ __launch_bounds__(kRbThreads) void nvfp4_reblock_kernel(const uint8_t *__restrict__ plain,
+                                                                  uint8_t *__restrict__ blocked,
+                                                                  ReblockParams p)
+{
+    __shared__ uint32_t tile_words[128 * kLdsPitch];
+    const int32_t t = threadIdx.x;
+    const int32_t wg = blockIdx.x % p.wg_per_rb;
+    const int64_t rbl = blockIdx.x / p.wg_per_rb;          // batch * nrb + row block
+    const int32_t l = (int32_t)(rbl / p.nrb), rb = (int32_t)(rbl % p.nrb);
+    const int32_t cb0 = wg * kTilesPerWg;
+    const uint8_t *in = plain + (int64_t)l * p.in_batch;
+    uint8_t *out = blocked + (int64_t)l * p.out_batch;
+
+    // read: 128 rows x kWordsPerRow words, 16 threads per row
+#pragma unroll
+    for (int i = 0; i < 128 * kWordsPerRow / kRbThreads; ++i) {
+        const int32_t e = t + i * kRbThreads;
+        const int32_t row = e / kWordsPerRow, wd = e % kWordsPerRow;
+        tile_words[row * kLdsPitch + wd] = load_word<WORDS>(in, p, rb * 128 + row, cb0 + wd);
+    }
+    __syncthreads();
+    // write: kTilesPerWg tiles of 32 lines; line (tile, r32) = rows r32 + 32*i4
+#pragma unroll
+    for (int i = 0; i < kTilesPerWg * 32 / kRbThreads; ++i) {
+        const int32_t e = t + i * kRbThreads;
+        const int32_t tl = e / 32, r32 = e % 32;
+        if (cb0 + tl < p.ncb) {
+            uint4_t v;
+            v.x = tile_words[(r32 + 0) * kLdsPitch + tl];
+            v.y = tile_words[(r32 + 32) * kLdsPitch + tl];
+            v.z = tile_words[(r32 + 64) * kLdsPitch + tl];
+            v.w = tile_words[(r32 + 96) * kLdsPitch + tl];
+            *(uint4_t *)(out + ((int64_t)rb * p.ncb + cb0 + tl) * 512 + r32 * 16) = v;
+        }
+    }
+}
+
+} // namespace
+
+extern "C" {
+
+size_t nvfp4_blocked_scales_bytes(int64_t rows, int64_t K, int64_t L)
+{
+    if (rows < 1 || K < 32 || K % 32 != 0 || L < 1 || rows > INT32_MAX / 2 || K / 16 > INT32_MAX / 2)
+        return 0;
+    const int64_t nrb = (rows + 127) / 128, ncb = (K / 16 + 3) / 4;
+    if (L > (INT64_C(1) << 62) / (nrb * ncb * 512))
+        return 0;
+    return (size_t)(L * nrb * ncb * 512);
+}
+
+nvfp4_status_t nvfp4_scales_to_blocked(const void *plain, void *blocked, int64_t rows, int64_t K,
+                                       int64_t L, void *stream)
+{
+    if (!plain || !blocked)
+        return NVFP4_ERR_NULL_POINTER;
+    if (nvfp4_blocked_scales_bytes(rows, K, L) == 0)
+        return NVFP4_ERR_INVALID_SHAPE;
+    if (((uintptr_t)blocked & 15) != 0)
+        return NVFP4_ERR_MISALIGNED;
+    ReblockParams p{};
+    p.rows = (int32_t)rows;
+    p.cols = (int32_t)(K / 16);
+    p.nrb = (int32_t)((rows + 127) / 128);
+    p.ncb = (p.cols + 3) / 4;
+    p.wg_per_rb = (p.ncb + kTilesPerWg - 1) / kTilesPerWg;
+    p.in_batch = rows * (K / 16);
+    p.out_batch = (int64_t)p.nrb * p.ncb * 512;
+    const int64_t grid = L * p.nrb * p.wg_per_rb;
+    if (grid > INT32_MAX)
+        return NVFP4_ERR_INVALID_SHAPE;
+    const bool words = p.cols % 4 == 0 && ((uintptr_t)plain & 3) == 0;
+    if (words)
+        hipLaunchKernelGGL(nvfp4_reblock_kernel<true>, dim3((uint32_t)grid), dim3(kRbThreads), 0,
+                           (hipStream_t)stream, (const uint8_t *)plain, (uint8_t *)blocked, p);
+    else
+        hipLaunchKernelGGL(nvfp4_reblock_kernel<false>, dim3((uint32_t)grid), dim3(kRbThreads), 0,
+                           (hipStream_t)stream, (const uint8_t *)plain, (uint8_t *)blocked, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        nvfp4_record_hip_error((int)e);
+        return NVFP4_ERR_HIP;
+    }
+    return NVFP4_OK;
+}
+
+} // extern "C"

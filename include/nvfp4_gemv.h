@@ -149,6 +149,29 @@ typedef struct {
 
 nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan);
 
+/*
+ * Device-side reblocking of plain scale factors into the 128x4 blocked layout
+ * (the transformation kernelbot NVFP4 GEMV submission 69953 performs with
+ * `to_blocked_batch` and submission 69575 with `blocked_transform_kernel`,
+ * here as one HIP kernel for all batches), so that callers holding plain
+ * scales can produce what nvfp4_gemv reads with sf_layout = NVFP4_SF_BLOCKED.
+ *
+ *   plain    uint8 [L][rows][K/16] E4M3 codes (rows = M for SFA, 1 for SFB)
+ *   blocked  uint8, nvfp4_blocked_scales_bytes(rows, K, L) bytes, written:
+ *            per batch ceil(rows/128)*ceil(K/64)*512 bytes, scale (r, kb) at
+ *            ((r/128)*ceil(K/64) + kb/4)*512 + (r%32)*16 + ((r%128)/32)*4 + kb%4;
+ *            padding bytes (r >= rows or kb >= K/16) are written as 0.
+ * Both are DEVICE pointers owned by the caller; blocked must be 16-byte
+ * aligned (plain has no alignment requirement) and the two must not overlap.
+ * Requirements: rows, L >= 1; K >= 32, K % 32 == 0. Errors are reported before
+ * any HIP call (nothing launched); the call only enqueues work on `stream`.
+ */
+nvfp4_status_t nvfp4_scales_to_blocked(const void *plain, void *blocked, int64_t rows, int64_t K,
+                                       int64_t L, void *stream);
+
+/* Bytes of the blocked layout for (rows, K, L); 0 for an invalid shape. */
+size_t nvfp4_blocked_scales_bytes(int64_t rows, int64_t K, int64_t L);
+
 /* Static description of a status code (never NULL). */
 const char *nvfp4_status_string(int status);
 

@@ -83,6 +83,8 @@ def _load():
     lib.nvo_gemv_rows.restype = ctypes.c_int
     lib.nvo_gemv_rows.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                   vp, i64, ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.nvo_reblock.restype = ctypes.c_int
+    lib.nvo_reblock.argtypes = [vp, i64, i64, i64, vp]
     _lib = lib
     return lib
 
@@ -117,6 +119,19 @@ def sf_offset(layout: int, r: int, kb: int, rows: int, nkb: int) -> int:
 
 def sf_batch_bytes(layout: int, rows: int, nkb: int) -> int:
     return _load().nvo_sf_batch_bytes(layout, rows, nkb)
+
+
+def reblock(plain, rows: int, K: int, L: int) -> np.ndarray:
+    """Plain scales [L][rows][K/16] -> blocked bytes [L][per-batch bytes],
+    padding 0 (the oracle of the device reblock)."""
+    plain = np.ascontiguousarray(plain, dtype=np.uint8)
+    if plain.size != L * rows * (K // 16):
+        raise ValueError("plain size mismatch")
+    per = sf_batch_bytes(BLOCKED, rows, K // 16)
+    out = np.zeros(L * per, np.uint8)
+    if _load().nvo_reblock(_ptr(plain), rows, K, L, _ptr(out)) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out.reshape(L, per)
 
 
 # ---------------------------------------------------------------- fp16

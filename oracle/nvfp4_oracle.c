@@ -139,6 +139,28 @@ int64_t nvo_sf_offset(int layout, int64_t r, int64_t kb, int64_t rows, int64_t n
                        : nvo_sf_offset_blocked(r, kb, rows, nkb);
 }
 
+/*
+ * Reblock plain scales [L][rows][K/16] into the blocked layout (submission
+ * 69953 `to_blocked_batch`, the map above): every scale is written to its
+ * blocked byte, every padding byte (row >= rows or column >= K/16) is 0.
+ * out holds L * nvo_sf_batch_bytes(1, rows, K/16) bytes. Returns 0, or -1 for
+ * invalid arguments.
+ */
+int nvo_reblock(const uint8_t *plain, int64_t rows, int64_t K, int64_t L, uint8_t *out)
+{
+    if (!plain || !out || rows < 1 || L < 1 || K < 32 || K % 32 != 0)
+        return -1;
+    const int64_t nkb = K / 16;
+    const int64_t in_batch = rows * nkb, out_batch = nvo_sf_batch_bytes(1, rows, nkb);
+    memset(out, 0, (size_t)(L * out_batch));
+    for (int64_t l = 0; l < L; ++l)
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t kb = 0; kb < nkb; ++kb)
+                out[l * out_batch + nvo_sf_offset_blocked(r, kb, rows, nkb)] =
+                    plain[l * in_batch + r * nkb + kb];
+    return 0;
+}
+
 /* ------------------------------------------------------- fp16 rounding */
 
 static int msb64(uint64_t x)

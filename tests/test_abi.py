@@ -189,3 +189,20 @@ def test_binding_checks_buffer_sizes():
 
     with pytest.raises(ValueError, match="a holds"):
         g.nvfp4_gemv(Fake(10), Fake(128), Fake(2048), Fake(16), Fake(256), 128, 256, 1, "plain")
+
+
+def test_blocked_scales_bytes():
+    assert g.nvfp4_blocked_scales_bytes(7168, 16384, 1) == 56 * 256 * 512
+    assert g.nvfp4_blocked_scales_bytes(1, 32, 3) == 3 * 512
+    assert g.nvfp4_blocked_scales_bytes(129, 96, 2) == 2 * 2 * 2 * 512
+    for bad in [(0, 32, 1), (1, 48, 1), (1, 32, 0), (1, 16, 1)]:
+        assert g.nvfp4_blocked_scales_bytes(*bad) == 0
+
+
+def test_reblock_validation_before_launch():
+    lib = g.lib()
+    assert lib.nvfp4_scales_to_blocked(None, A16, 128, 256, 1, None) == g.NVFP4_ERR_NULL_POINTER
+    assert lib.nvfp4_scales_to_blocked(A16, None, 128, 256, 1, None) == g.NVFP4_ERR_NULL_POINTER
+    assert lib.nvfp4_scales_to_blocked(A16, A16 + 0x1000, 128, 48, 1, None) == g.NVFP4_ERR_INVALID_SHAPE
+    assert lib.nvfp4_scales_to_blocked(A16, A16 + 0x1000, 0, 256, 1, None) == g.NVFP4_ERR_INVALID_SHAPE
+    assert lib.nvfp4_scales_to_blocked(A16, A16 + 0x1008, 128, 256, 1, None) == g.NVFP4_ERR_MISALIGNED

@@ -1,0 +1,62 @@
+"""CPU mirror of the reblock kernel's index arithmetic (nvfp4_reblock.hip),
+run over its whole grid before it runs on a GPU: every plain read and every
+blocked write is inside its buffer, every blocked byte is written exactly once,
+and the bytes written are the view chain's (padding 0). Keep in step with the
+kernel: 256 threads, 16 tiles per workgroup, 16 words per row in LDS."""
+import numpy as np
+import pytest
+
+import block_scaled_fp4_gemv_amd as g
+import synth
+
+THREADS, TILES = 256, 16
+
+
+def emulate(plain, rows, K, L):
+    cols = K // 16
+    nrb, ncb = -(-rows // 128), -(-cols // 4)
+    wg_per_rb = -(-ncb // TILES)
+    out_batch = nrb * ncb * 512
+    out = np.full(L * out_batch, 0xAB, np.uint8)
+    writes = np.zeros(L * out_batch, np.int64)
+    flat = plain.reshape(-1)
+    t = np.arange(THREADS)
+    for bid in range(L * nrb * wg_per_rb):
+        wg, rbl = bid % wg_per_rb, bid // wg_per_rb
+        l, rb = rbl // nrb, rbl % nrb
+        assert l < L
+        cb0 = wg * TILES
+        words = np.zeros((128, TILES), np.uint32)
+        for i in range(128 * TILES // THREADS):
+            e = t + i * THREADS
+            row, wd = e // TILES, e % TILES
+            r, cb = rb * 128 + row, cb0 + wd
+            for rr, cc, rw, w in zip(r, cb, row, wd):
+                if rr >= rows or 4 * cc >= cols:
+                    continue
+                n = min(4, cols - 4 * cc)
+                src = l * rows * cols + rr * cols + 4 * cc
+                assert 0 <= src and src + n <= flat.size, "plain read outside the buffer"
+                words[rw, w] = int.from_bytes(flat[src:src + n].tobytes(), "little")
+        for i in range(TILES * 32 // THREADS):
+            e = t + i * THREADS
+            tl, r32 = e // 32, e % 32
+            for a, b in zip(tl, r32):
+                if cb0 + a >= ncb:
+                    continue
+                dst = l * out_batch + (rb * ncb + cb0 + a) * 512 + b * 16
+                assert 0 <= dst and dst + 16 <= out.size, "blocked write outside the buffer"
+                v = np.array([words[b + 32 * i4, a] for i4 in range(4)], np.uint32)
+                out[dst:dst + 16] = v.view(np.uint8)
+                writes[dst:dst + 16] += 1
+    return out.reshape(L, out_batch), writes
+
+
+@pytest.mark.parametrize("rows,K,L", [(1, 32, 1), (1, 96, 2), (127, 4096, 1), (128, 2048, 2),
+                                      (300, 4128, 1), (129, 32, 3), (7, 1056, 2)])
+def test_reblock_kernel_indexing(rows, K, L):
+    plain = np.random.default_rng(rows * K + L).integers(0, 256, (L, rows, K // 16), dtype=np.uint8)
+    out, writes = emulate(plain, rows, K, L)
+    assert np.all(writes == 1), "each blocked byte is written exactly once"
+    np.testing.assert_array_equal(out, synth.to_blocked(plain, pad=0))
+    assert out.size == g.nvfp4_blocked_scales_bytes(rows, K, L)

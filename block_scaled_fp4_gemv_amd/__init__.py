@@ -34,12 +34,15 @@ NVFP4_ERR_INVALID_LAYOUT = 4
 NVFP4_ERR_WORKSPACE = 5
 NVFP4_ERR_HIP = 6
 NVFP4_ERR_INVALID_SCALE = 7
+NVFP4_ERR_INVALID_STRIDE = 8
 
 EXPORTED_SYMBOLS = (
     "nvfp4_gemv",
     "nvfp4_gemv_workspace_bytes",
     "nvfp4_gemv_ex",
     "nvfp4_gemv_scaled",
+    "nvfp4_gemv_strided",
+    "nvfp4_gemv_dense_strides",
     "nvfp4_gemv_plan",
     "nvfp4_scales_to_blocked",
     "nvfp4_blocked_scales_bytes",
@@ -55,6 +58,18 @@ class Nvfp4Error(RuntimeError):
         if status == NVFP4_ERR_HIP:
             msg += f" (hipError_t {lib().nvfp4_last_hip_error()})"
         super().__init__(f"{where}: {msg} [status {status}]")
+
+
+class Strides(ctypes.Structure):
+    """nvfp4_strides_t: byte strides (c_batch in float16 elements)."""
+    _fields_ = [("a_row", ctypes.c_int64), ("a_batch", ctypes.c_int64),
+                ("b_batch", ctypes.c_int64),
+                ("sfa_row", ctypes.c_int64), ("sfa_batch", ctypes.c_int64),
+                ("sfb_batch", ctypes.c_int64),
+                ("c_batch", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class Plan(ctypes.Structure):
@@ -90,6 +105,11 @@ def lib():
     L.nvfp4_gemv_scaled.restype = i32
     L.nvfp4_gemv_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_float, vp,
                                     ctypes.c_size_t, vp]
+    L.nvfp4_gemv_strided.restype = i32
+    L.nvfp4_gemv_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.POINTER(Strides),
+                                     ctypes.c_float, vp, ctypes.c_size_t, vp]
+    L.nvfp4_gemv_dense_strides.restype = None
+    L.nvfp4_gemv_dense_strides.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Strides)]
     L.nvfp4_gemv_workspace_bytes.restype = ctypes.c_size_t
     L.nvfp4_gemv_workspace_bytes.argtypes = [i64, i64, i64]
     L.nvfp4_gemv_plan.restype = i32
@@ -208,6 +228,40 @@ def nvfp4_gemv_scaled(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, alph
                                  workspace_bytes, _stream_handle(stream))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemv_scaled")
+
+
+def nvfp4_gemv_dense_strides(M: int, K: int, L: int, sf_layout) -> dict:
+    st = Strides()
+    lib().nvfp4_gemv_dense_strides(M, K, L, layout_id(sf_layout), ctypes.byref(st))
+    return st.as_dict()
+
+
+def _raw_ptr(x):
+    """Device pointer of a torch tensor (any strides: the library reads through
+    the strides it is given), or a raw int."""
+    if x is None or isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("operands must be device tensors")
+    return x.data_ptr()
+
+
+def nvfp4_gemv_strided(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, strides: dict,
+                       alpha: float = 1.0, workspace=None, workspace_bytes: int | None = None,
+                       stream=None) -> None:
+    """Enqueue c = fp16(alpha * GEMV) over strided operands: ``strides`` holds
+    the fields of nvfp4_strides_t (bytes; c_batch in elements). The tensors
+    are passed by base pointer: the library reads and writes through the
+    strides, so each tensor must cover what they address."""
+    st = Strides(**strides)
+    pw, nw = _ptr_and_bytes(workspace)
+    if workspace_bytes is None:
+        workspace_bytes = nw or 0
+    rc = lib().nvfp4_gemv_strided(_raw_ptr(a), _raw_ptr(b), _raw_ptr(sfa), _raw_ptr(sfb), _raw_ptr(c),
+                                  M, K, L, layout_id(sf_layout), ctypes.byref(st), float(alpha), pw,
+                                  workspace_bytes, _stream_handle(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_gemv_strided")
 
 
 def nvfp4_gemv_plan(M: int, K: int, L: int) -> dict:

@@ -95,9 +95,14 @@ struct Params {
     int32_t ns;           // slots per batch that hold at least one row
     int32_t stage_bytes;  // LDS bytes for the staged scales (whole direct-to-LDS loads)
     int32_t wide_plain;   // plain scales staged in 16-byte units
-    int64_t sfa_batch;    // bytes per batch of SFA
-    int64_t sfb_batch;    // bytes per batch of SFB
-    int64_t a_bytes;      // bytes of A (all batches)
+    int32_t a_row;        // bytes between rows of A (a multiple of 16)
+    int64_t a_batch;      // bytes between batches of A
+    int64_t a_extent;     // bytes from A to one past its last byte
+    int64_t b_batch;      // bytes between batches of B
+    int64_t sfa_row;      // bytes between rows of plain SFA
+    int64_t sfa_batch;    // bytes between batches of SFA
+    int64_t sfb_batch;    // bytes between batches of SFB
+    int64_t c_batch;      // float16 elements between batches of C
     float alpha;          // global scale, applied to the float32 row sum before rounding
     uint32_t *counters;   // tickets [L][P] when S > 1
     float *partials;      // [L*M][S] when S > 1
@@ -264,10 +269,11 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const int wig = WPG > 1 ? j >> 6 : 0;                 // wave index inside the row group
     const bool leader = (lane % RED) == RED - 1;           // holds the group sum after group_sum
 
-    const int64_t abatch = (int64_t)l * M;
+    const int64_t abatch = (int64_t)l * M;                 // row index base of the split-K partials
+    const int64_t cbatch = (int64_t)l * p.c_batch;
     const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
     const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
-    const uint8_t *b_l = B + (int64_t)l * (K >> 1);
+    const uint8_t *b_l = B + (int64_t)l * p.b_batch;
     uint8_t *stage = lds;                                  // staged scales of the segment
     float *part = (float *)(lds + p.stage_bytes);          // [nq][WPG] per-wave row sums
 
@@ -275,9 +281,9 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     // first 128-row block: 32-bit lane offsets (the rows of one workgroup lie
     // within a few blocks).
     const int32_t row_base = (first >> 5) << 7;
-    const int64_t a_begin = (abatch + row_base) * (int64_t)(K >> 1);
+    const int64_t a_begin = (int64_t)l * p.a_batch + (int64_t)row_base * p.a_row;
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A + a_begin), (short)0, (int)min(p.a_bytes - a_begin, (int64_t)0x7FFFFFFF),
+        (void *)(A + a_begin), (short)0, (int)min(p.a_extent - a_begin, (int64_t)0x7FFFFFFF),
         kBufferFlags);
 
     const int32_t NR = (nq + G - 1) / G;                   // row rounds per group
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                         src = sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + mjc) * 512 + (sg & 31) * 16;
                     } else {
                         const int32_t r = min(slot_row(first, mjc), M - 1);
-                        src = sfa_l + (int64_t)r * nkb + 2 * c0 + 16 * mn;
+                        src = sfa_l + (int64_t)r * p.sfa_row + 2 * c0 + 16 * mn;
                     }
                     __builtin_amdgcn_global_load_lds((const void *)src,
                                                      (__attribute__((address_space(3))) void *)(stage + i * kDmaBytes),
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 for (int32_t it = lane; it < nq * nck; it += 64) {
                     const int32_t q = it / nck, c = it % nck;
                     const int32_t r = min(slot_row(first, q), M - 1);
-                    *(uint16_t *)(stage + 2 * it) = *(const uint16_t *)(sfa_l + (int64_t)r * nkb + 2 * (c0 + c));
+                    *(uint16_t *)(stage + 2 * it) = *(const uint16_t *)(sfa_l + (int64_t)r * p.sfa_row + 2 * (c0 + c));
                 }
             }
             __syncthreads();                               // publish the staged scales
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         auto row_off = [&](int32_t n) -> uint32_t {
             const int32_t q = min(grp + G * n, nq - 1);
             const int32_t r = min(slot_row(first, q), M - 1);
-            return (uint32_t)(r - row_base) * (uint32_t)(K >> 1);
+            return (uint32_t)(r - row_base) * (uint32_t)p.a_row;
         };
         // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
         // the end read a clamped (valid) chunk so that every load is
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
 #pragma unroll
                 for (int w = 1; w < WPG; ++w)
                     v += part[q * WPG + w];
-                C[abatch + r] = f16_bits(v * p.alpha);
+                C[cbatch + r] = f16_bits(v * p.alpha);
             }
         }
         return;
@@ -550,7 +556,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
             float v = 0.0f;
             for (int k = 0; k < p.S; ++k)
                 v += __hip_atomic_load(pp + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            C[abatch + r] = f16_bits(v * p.alpha);
+            C[cbatch + r] = f16_bits(v * p.alpha);
         }
     }
 }
@@ -729,9 +735,44 @@ nvfp4_status_t validate(const void *a, const void *b, const void *sfa, const voi
     return NVFP4_OK;
 }
 
+// Dense operand strides (the layouts of the header).
+nvfp4_strides_t dense_strides(int64_t M, int64_t K, int64_t L, int sf_layout)
+{
+    nvfp4_strides_t s{};
+    const int64_t nkb = K / 16, ncb = cdiv(nkb, 4);
+    s.a_row = K / 2;
+    s.a_batch = M * (K / 2);
+    s.b_batch = K / 2;
+    s.sfa_row = nkb;
+    s.sfa_batch = sf_layout == NVFP4_SF_BLOCKED ? cdiv(M, 128) * ncb * 512 : M * nkb;
+    s.sfb_batch = sf_layout == NVFP4_SF_BLOCKED ? ncb * 512 : nkb;
+    s.c_batch = M;
+    (void)L;
+    return s;
+}
+
+// Strides the kernel can take (see nvfp4_gemv_strided in the header).
+nvfp4_status_t check_strides(const nvfp4_strides_t &s, int64_t M, int64_t K, int64_t L, int sf_layout,
+                             const Plan &pl)
+{
+    const int64_t big = INT64_C(1) << 40;
+    auto in = [&](int64_t v, int64_t lo, int64_t mult) { return v >= lo && v < big && v % mult == 0; };
+    const bool blocked = sf_layout == NVFP4_SF_BLOCKED;
+    if (!in(s.a_row, K / 2, 16) || !in(s.a_batch, 0, 16) || !in(s.b_batch, 0, 16) ||
+        !in(s.sfa_batch, 0, blocked ? 16 : 2) || !in(s.sfb_batch, 0, blocked ? 16 : 2) ||
+        (!blocked && !in(s.sfa_row, K / 16, 2)) || !in(s.c_batch, L > 1 ? M : 0, 1))
+        return NVFP4_ERR_INVALID_STRIDE;
+    // a workgroup's A offsets are 32-bit: its rows lie in at most
+    // ceil(spw/32) + 1 blocks of 128 rows
+    const int64_t span = (cdiv(pl.spw, 32) + 1) * 128;
+    if (span * s.a_row + K / 2 > INT64_C(0x7FFFFFFF))
+        return NVFP4_ERR_INVALID_STRIDE;
+    return NVFP4_OK;
+}
+
 nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void *sfb, void *c,
                       int64_t M, int64_t K, int64_t L, int sf_layout, float alpha, const Plan &pl,
-                      void *ws, hipStream_t st)
+                      const nvfp4_strides_t &sd, void *ws, hipStream_t st)
 {
     Params p{};
     p.alpha = alpha;
@@ -744,16 +785,16 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
     p.spw = pl.spw;
     p.ns = pl.ns;
     p.stage_bytes = pl.stage_bytes;
-    p.wide_plain = pl.wide_plain;
-    p.a_bytes = L * M * (K / 2);
-    const int64_t nkb = K / 16, ncb = cdiv(nkb, 4);
-    if (sf_layout == NVFP4_SF_PLAIN) {
-        p.sfa_batch = M * nkb;
-        p.sfb_batch = nkb;
-    } else {
-        p.sfa_batch = cdiv(M, 128) * ncb * 512;
-        p.sfb_batch = ncb * 512;
-    }
+    // plain scales are staged 16 bytes at a time only from 16-byte aligned rows
+    p.wide_plain = pl.wide_plain && sd.sfa_row % 16 == 0 && sd.sfa_batch % 16 == 0;
+    p.a_row = (int32_t)sd.a_row;
+    p.a_batch = sd.a_batch;
+    p.a_extent = (L - 1) * sd.a_batch + (M - 1) * sd.a_row + K / 2;
+    p.b_batch = sd.b_batch;
+    p.sfa_row = sd.sfa_row;
+    p.sfa_batch = sd.sfa_batch;
+    p.sfb_batch = sd.sfb_batch;
+    p.c_batch = sd.c_batch;
     if (pl.S > 1) {
         p.counters = (uint32_t *)ws;
         p.partials = (float *)((char *)ws + kCounterBytes);
@@ -830,7 +871,8 @@ nvfp4_status_t nvfp4_gemv(const void *a, const void *b, const void *sfa, const v
     void *ws = nullptr;
     if (pl.ws_total > 0 && (st = device_workspace(pl.ws_total, &ws)) != NVFP4_OK)
         return st;
-    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, ws, (hipStream_t)stream);
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, dense_strides(M, K, L, sf_layout), ws,
+                  (hipStream_t)stream);
 }
 
 size_t nvfp4_gemv_workspace_bytes(int64_t M, int64_t K, int64_t L)
@@ -851,7 +893,8 @@ nvfp4_status_t nvfp4_gemv_ex(const void *a, const void *b, const void *sfa, cons
     if (pl.ws_total > 0 &&
         (!workspace || workspace_bytes < pl.ws_total || !aligned(workspace, kWsAlign)))
         return NVFP4_ERR_WORKSPACE;
-    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, workspace, (hipStream_t)stream);
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, dense_strides(M, K, L, sf_layout),
+                  workspace, (hipStream_t)stream);
 }
 
 nvfp4_status_t nvfp4_gemv_scaled(const void *a, const void *b, const void *sfa, const void *sfb,
@@ -862,9 +905,26 @@ nvfp4_status_t nvfp4_gemv_scaled(const void *a, const void *b, const void *sfa, 
     nvfp4_status_t st = validate(a, b, sfa, sfb, c, M, K, L, sf_layout);
     if (st != NVFP4_OK)
         return st;
+    const nvfp4_strides_t sd = dense_strides(M, K, L, sf_layout);
+    return nvfp4_gemv_strided(a, b, sfa, sfb, c, M, K, L, sf_layout, &sd, alpha, workspace,
+                              workspace_bytes, stream);
+}
+
+nvfp4_status_t nvfp4_gemv_strided(const void *a, const void *b, const void *sfa, const void *sfb,
+                                  void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
+                                  const nvfp4_strides_t *strides, float alpha, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    nvfp4_status_t st = validate(a, b, sfa, sfb, c, M, K, L, sf_layout);
+    if (st != NVFP4_OK)
+        return st;
+    if (!strides)
+        return NVFP4_ERR_NULL_POINTER;
     if (!std::isfinite(alpha))
         return NVFP4_ERR_INVALID_SCALE;
     const Plan pl = make_plan(M, K, L);
+    if ((st = check_strides(*strides, M, K, L, sf_layout, pl)) != NVFP4_OK)
+        return st;
     void *ws = workspace;
     if (pl.ws_total > 0) {
         if (!workspace) {
@@ -876,7 +936,13 @@ nvfp4_status_t nvfp4_gemv_scaled(const void *a, const void *b, const void *sfa, 
             return NVFP4_ERR_WORKSPACE;
         }
     }
-    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, pl, ws, (hipStream_t)stream);
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, pl, *strides, ws, (hipStream_t)stream);
+}
+
+void nvfp4_gemv_dense_strides(int64_t M, int64_t K, int64_t L, int sf_layout, nvfp4_strides_t *strides)
+{
+    if (strides)
+        *strides = dense_strides(M, K, L, sf_layout);
 }
 
 nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan)
@@ -908,6 +974,7 @@ const char *nvfp4_status_string(int status)
     case NVFP4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case NVFP4_ERR_HIP: return "HIP runtime error";
     case NVFP4_ERR_INVALID_SCALE: return "global scale alpha is not finite";
+    case NVFP4_ERR_INVALID_STRIDE: return "operand stride out of range or misaligned";
     default: return "unknown status";
     }
 }

@@ -68,7 +68,8 @@ typedef enum {
     NVFP4_ERR_INVALID_LAYOUT = 4,   /* sf_layout is not an nvfp4_sf_layout_t       */
     NVFP4_ERR_WORKSPACE = 5,        /* workspace missing, misaligned or too small  */
     NVFP4_ERR_HIP = 6,              /* a HIP call failed; see nvfp4_last_hip_error */
-    NVFP4_ERR_INVALID_SCALE = 7     /* the global scale alpha is NaN or infinite   */
+    NVFP4_ERR_INVALID_SCALE = 7,    /* the global scale alpha is NaN or infinite   */
+    NVFP4_ERR_INVALID_STRIDE = 8    /* an operand stride is out of range or misaligned */
 } nvfp4_status_t;
 
 /*
@@ -125,6 +126,49 @@ nvfp4_status_t nvfp4_gemv_scaled(const void *a, const void *b, const void *sfa, 
                                  void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
                                  float alpha, void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/*
+ * Operand strides, for callers whose tensors are not densely packed (the
+ * pages' harness, kernelbot NVFP4 GEMV submission 103289, hands B over with
+ * its N dimension padded to 128 rows, so B's batch stride is 128*K/2 bytes;
+ * submission 69575 reads plain scales through arbitrary row and batch
+ * strides). Inside a row everything stays contiguous. Byte strides except
+ * c_batch, which counts float16 elements:
+ *   a_row      between rows m, m+1 of A        >= K/2, multiple of 16
+ *   a_batch    between batches of A            >= 0,   multiple of 16
+ *   b_batch    between batches of B            >= 0,   multiple of 16
+ *   sfa_row    between rows of SFA (plain layout only; ignored for blocked,
+ *              whose tiles fix it)             >= K/16, even
+ *   sfa_batch  between batches of SFA          >= 0, even (plain) / multiple of 16 (blocked)
+ *   sfb_batch  between batches of SFB          >= 0, even (plain) / multiple of 16 (blocked)
+ *   c_batch    between batches of C, elements  >= M when L > 1 (outputs must not overlap)
+ * A batch stride of 0 broadcasts one input to every batch. All strides are
+ * below 2^40, and the rows of A that one workgroup reads must lie within 2^31
+ * bytes: (ceil(rows_per_wg/128) + 1) * 128 * a_row + K/2 < 2^31, with
+ * rows_per_wg from nvfp4_gemv_plan (about a_row <= 2^21 for any shape).
+ */
+typedef struct {
+    int64_t a_row, a_batch;
+    int64_t b_batch;
+    int64_t sfa_row, sfa_batch;
+    int64_t sfb_batch;
+    int64_t c_batch;
+} nvfp4_strides_t;
+
+/* The dense strides of the layouts above (what nvfp4_gemv assumes). */
+void nvfp4_gemv_dense_strides(int64_t M, int64_t K, int64_t L, int sf_layout,
+                              nvfp4_strides_t *strides);
+
+/*
+ * nvfp4_gemv_scaled with operand strides (`strides` must not be NULL):
+ * pointers, alignment, alpha and workspace as for nvfp4_gemv_scaled;
+ * NVFP4_ERR_INVALID_STRIDE, nothing launched, for strides outside the rules
+ * above. Results are bit-identical to the dense call on the same values.
+ */
+nvfp4_status_t nvfp4_gemv_strided(const void *a, const void *b, const void *sfa, const void *sfb,
+                                  void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
+                                  const nvfp4_strides_t *strides, float alpha, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * Launch plan chosen for a shape (for tests and reports). Returns NVFP4_OK and

@@ -162,7 +162,7 @@ def test_plan_rejects_bad_shape():
 
 
 def test_status_strings():
-    for st in range(0, 8):
+    for st in range(0, 9):
         assert g.status_string(st)
     assert g.status_string(1234) == "unknown status"
 
@@ -206,3 +206,45 @@ def test_reblock_validation_before_launch():
     assert lib.nvfp4_scales_to_blocked(A16, A16 + 0x1000, 128, 48, 1, None) == g.NVFP4_ERR_INVALID_SHAPE
     assert lib.nvfp4_scales_to_blocked(A16, A16 + 0x1000, 0, 256, 1, None) == g.NVFP4_ERR_INVALID_SHAPE
     assert lib.nvfp4_scales_to_blocked(A16, A16 + 0x1008, 128, 256, 1, None) == g.NVFP4_ERR_MISALIGNED
+
+
+def strided_call(layout=1, M=1000, K=4096, L=3, **over):
+    sd = g.nvfp4_gemv_dense_strides(M, K, L, layout)
+    sd.update(over)
+    st = g.Strides(**sd)
+    return g.lib().nvfp4_gemv_strided(OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"],
+                                      OK_ARGS["c"], M, K, L, layout, ctypes.byref(st), 1.0, None, 0, None)
+
+
+def test_dense_strides():
+    assert g.nvfp4_gemv_dense_strides(1000, 4096, 3, 0) == dict(
+        a_row=2048, a_batch=1000 * 2048, b_batch=2048, sfa_row=256, sfa_batch=1000 * 256,
+        sfb_batch=256, c_batch=1000)
+    d = g.nvfp4_gemv_dense_strides(1000, 4096, 3, 1)
+    assert d["sfa_batch"] == 8 * 64 * 512 and d["sfb_batch"] == 64 * 512
+
+
+@pytest.mark.parametrize("layout,over", [
+    (1, dict(a_row=2047)), (1, dict(a_row=2056)), (1, dict(a_batch=8)), (1, dict(b_batch=-16)),
+    (1, dict(sfa_batch=8)), (1, dict(sfb_batch=4)), (1, dict(c_batch=999)),
+    (0, dict(sfa_row=255)), (0, dict(sfa_row=257)), (0, dict(sfa_batch=3)), (0, dict(sfb_batch=1)),
+    (1, dict(a_row=2 ** 24)), (1, dict(a_batch=2 ** 41))])
+def test_strided_rejects_bad_strides(layout, over):
+    assert strided_call(layout, **over) == g.NVFP4_ERR_INVALID_STRIDE
+
+
+def test_strided_null_strides_and_order():
+    lib = g.lib()
+    args = (OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"], OK_ARGS["c"], 128, 256, 1, 0)
+    assert lib.nvfp4_gemv_strided(*args, None, 1.0, None, 0, None) == g.NVFP4_ERR_NULL_POINTER
+    # shape errors come first, then NULL strides
+    bad = (OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"], OK_ARGS["c"], 128, 48, 1, 0)
+    assert lib.nvfp4_gemv_strided(*bad, None, 1.0, None, 0, None) == g.NVFP4_ERR_INVALID_SHAPE
+
+
+def test_strided_cases_pass_validation():
+    from test_kernel_bounds import STRIDED
+    for M, K, L, layout, over in STRIDED:
+        st = strided_call(layout, M, K, L, **over)
+        assert st not in (g.NVFP4_ERR_INVALID_STRIDE, g.NVFP4_ERR_INVALID_SHAPE, g.NVFP4_ERR_MISALIGNED), \
+            (M, K, L, layout, over)

@@ -51,9 +51,10 @@ def sf_offset(layout, r, kb, nkb, ncb):
 
 
 def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREADS, cpl=CPL,
-                prefetch=PREFETCH, max_tickets=MAX_TICKETS):
+                prefetch=PREFETCH, max_tickets=MAX_TICKETS, strides=None):
     """Walk the whole grid of one launch. ``plan``/``workspace_bytes`` default
-    to the built library's; the constants can be overridden to check a variant."""
+    to the built library's; the constants can be overridden to check a variant.
+    ``strides`` (nvfp4_strides_t fields) default to the dense layout."""
     THREADS, CPL, PREFETCH = threads, cpl, prefetch
     p = (plan or g.nvfp4_gemv_plan)(M, K, L)
     ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
@@ -69,18 +70,30 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     stb = stage_bytes(lpr, spw)
     assert lds_bytes == stb + 4 * spw * WPG * 4
     assert lds_bytes <= 64 * 1024
-    wide_plain = nchunks % 8 == 0 and kc % 8 == 0
+    sd = strides or g.nvfp4_gemv_dense_strides(M, K, L, layout)
+    a_row, a_bat, b_bat, c_bat = sd["a_row"], sd["a_batch"], sd["b_batch"], sd["c_batch"]
+    sfa_row, sfa_bat, sfb_bat = sd["sfa_row"], sd["sfa_batch"], sd["sfb_batch"]
+    wide_plain = nchunks % 8 == 0 and kc % 8 == 0 and sfa_row % 16 == 0 and sfa_bat % 16 == 0
     direct = layout == 0 and not wide_plain
-    a_bytes, b_size = L * M * K // 2, L * K // 2
-    sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512
+    # extents: one past the last byte each operand's strides address
+    a_bytes = (L - 1) * a_bat + (M - 1) * a_row + K // 2
+    b_size = (L - 1) * b_bat + K // 2
+    sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512     # dense bytes of one batch
     sfb_batch = nkb if layout == 0 else ncb * 512
-    valid_sfa = np.zeros(sfa_batch, bool)       # bytes that hold a real scale
+    sfa_size = (L - 1) * sfa_bat + ((M - 1) * sfa_row + nkb if layout == 0 else sfa_batch)
+    sfb_size = (L - 1) * sfb_bat + sfb_batch
+
+    def sfa_addr(l, r, kb):                     # global byte of scale (r, kb) of batch l
+        if layout == 0:
+            return l * sfa_bat + r * sfa_row + kb
+        return l * sfa_bat + sf_offset(1, r, kb, nkb, ncb)
+    valid_sfa = np.zeros(sfa_batch, bool)       # bytes that hold a real scale (dense batch)
     rr, kk = np.meshgrid(np.arange(M), np.arange(nkb), indexing="ij")
     valid_sfa[sf_offset(layout, rr, kk, nkb, ncb)] = True
     valid_sfb = np.zeros(sfb_batch, bool)
     valid_sfb[sf_offset(layout, np.zeros(nkb, np.int64), np.arange(nkb), nkb, ncb)] = True
 
-    written = np.zeros(L * M, np.int64)
+    written = np.zeros((L - 1) * c_bat + M, np.int64)
     lids = xcd_remap(np.arange(n_wg), n_wg)
     assert np.array_equal(np.sort(lids), np.arange(n_wg)), "remap is not a bijection"
     tid = np.arange(THREADS)
@@ -98,7 +111,7 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
         c_begin, c_end = s * kc, min(s * kc + kc, nchunks)
         assert c_end > c_begin
         row_base = (first >> 5) << 7
-        a_begin = (l * M + row_base) * (K // 2)
+        a_begin = l * a_bat + row_base * a_row
         num_records = min(a_bytes - a_begin, 2 ** 31 - 1)
         nsteps = cdiv(nq, G) * CPL
         rows_all = slot_row(first, np.arange(nq))
@@ -110,8 +123,9 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                 q = np.minimum(grp + G * (t // CPL), nq - 1)
                 r = np.minimum(slot_row(first, q), M - 1)
                 ci = c0 + np.minimum(j + (t % CPL) * lpr, nck - 1)
-                off = (r - row_base) * (K // 2) + ci * 16
+                off = (r - row_base) * a_row + ci * 16
                 assert off.min() >= 0 and (off + 16).max() <= num_records, "A read outside the resource"
+                assert (off + 16).max() < 2 ** 31, "A offset beyond 32 bits"
             # ---- staging wave: LDS byte -> global scale byte
             ncb_seg, cb0, units = (nck + 1) >> 1, c0 >> 1, nck >> 3
             lds_src = np.full(stb, -1, np.int64)
@@ -124,18 +138,19 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                     it = i * 64 + lane              # past the end: the major index is clamped
                     if layout == 1:
                         sg, cb = first + it % nslots, np.minimum(it // nslots, ncb_seg - 1)
-                        src = ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
+                        src = l * sfa_bat + ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
                     else:
                         q, u = np.minimum(it // units, nq - 1), it % units
                         r = np.minimum(slot_row(first, q), M - 1)
                         assert (2 * c0 + 16 * u + 16).max() <= nkb
-                        src = r * nkb + 2 * c0 + 16 * u
-                    assert src.min() >= 0 and (src + 16).max() <= sfa_batch, "SFA read outside the batch"
+                        src = l * sfa_bat + r * sfa_row + 2 * c0 + 16 * u
+                        assert (src % 16 == 0).all(), "16-byte staging copy from an unaligned address"
+                    assert src.min() >= 0 and (src + 16).max() <= sfa_size, "SFA read outside the tensor"
                     dst = i * DMA_BYTES + lane * 16
                     assert (dst + 16).max() <= stb, "staged item outside the staging area"
                     for b in range(16):
                         dst_all.append(dst + b)
-                        src_all.append(l * sfa_batch + src + b)
+                        src_all.append(src + b)
                 dst_cat = np.concatenate(dst_all)
                 assert np.unique(dst_cat).size == dst_cat.size, "two staging lanes write one LDS byte"
                 lds_src[dst_cat] = np.concatenate(src_all)
@@ -143,18 +158,19 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                 it = np.arange(nq * nck)
                 q, c = it // nck, it % nck
                 r = np.minimum(slot_row(first, q), M - 1)
-                src = l * sfa_batch + r * nkb + 2 * (c0 + c)
-                assert src.min() >= 0 and (src + 2).max() <= L * sfa_batch
+                src = l * sfa_bat + r * sfa_row + 2 * (c0 + c)
+                assert src.min() >= 0 and (src + 2).max() <= sfa_size
+                assert (src % 2 == 0).all()
                 assert (2 * it + 2).max() <= stb
                 lds_src[2 * it] = src
                 lds_src[2 * it + 1] = src + 1
             # ---- b': B chunk and its two SFB scales
             for k in range(CPL):
                 ci = c0 + np.minimum(j + k * lpr, nck - 1)
-                boff = l * (K // 2) + ci * 16
-                assert boff.min() >= 0 and (boff + 16).max() <= b_size
+                boff = l * b_bat + ci * 16
+                assert boff.min() >= 0 and (boff + 16).max() <= b_size and (boff % 16 == 0).all()
                 so = sf_offset(layout, np.zeros_like(ci), 2 * ci, nkb, ncb)
-                assert (so + 1).max() < sfb_batch
+                assert (so + 1).max() < sfb_batch and (l * sfb_bat + so + 2).max() <= sfb_size
                 assert valid_sfb[so].all() and valid_sfb[so + 1].all()
 
             # ---- computing waves: lane j reads, for its chunk k and round row q,
@@ -173,21 +189,24 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
             if qs.size:
                 qq, cl, b = np.meshgrid(qs, np.arange(nck), np.arange(2), indexing="ij")
                 rq = rows_all[qq]
-                want = l * sfa_batch + sf_offset(layout, rq, 2 * (c0 + cl) + b, nkb, ncb)
+                want = sfa_addr(l, rq, 2 * (c0 + cl) + b)
                 got = lds_src[staged_at(qq, cl) + b]
                 assert np.array_equal(got, want), "staged scales do not match what the compute reads"
-                assert valid_sfa[want - l * sfa_batch].all()
+                assert valid_sfa[sf_offset(layout, rq, 2 * (c0 + cl) + b, nkb, ncb)].all()
         # ---- outputs
         real = rows_all[rows_all < M]
         if S == 1 or s == S - 1:
-            np.add.at(written, l * M + real, 1)
+            np.add.at(written, l * c_bat + real, 1)
         if S > 1:
             assert P * L <= max_tickets, "more tickets than the ticket region holds"
             ws_part = cdiv(L * M * S * 4, 256) * 256
             assert ws_bytes == 4 * max_tickets + ws_part
             assert ((l * M + real) * S + s).max() < L * M * S
             assert l * P + tile < P * L
-    assert np.all(written == 1), "some output row is written zero or several times"
+    expect = np.zeros_like(written)
+    for l in range(L):
+        expect[l * c_bat + np.arange(M)] += 1
+    assert np.array_equal(written, expect), "some output row is written zero or several times"
 
 
 SHAPES = sorted({(w.M, w.K, w.L) for w in synth.ALL} |
@@ -204,3 +223,26 @@ SHAPES = sorted({(w.M, w.K, w.L) for w in synth.ALL} |
 @pytest.mark.parametrize("layout", [0, 1])
 def test_kernel_addresses_in_bounds(M, K, L, layout):
     check_shape(M, K, L, layout)
+
+
+def strided(M, K, L, layout, **over):
+    sd = g.nvfp4_gemv_dense_strides(M, K, L, layout)
+    sd.update(over)
+    return sd
+
+
+STRIDED = [  # (M, K, L, layout, stride overrides)
+    (300, 4128, 2, 0, dict(a_row=2080, a_batch=300 * 2080 + 48, b_batch=128 * 2064, sfa_row=272,
+                           sfa_batch=300 * 272 + 16, sfb_batch=272, c_batch=301)),
+    (300, 4128, 2, 0, dict(sfa_row=260, sfa_batch=300 * 260 + 2, sfb_batch=258)),   # odd-16 rows: 2-byte path
+    (1000, 4096, 3, 1, dict(a_row=2048 + 512, a_batch=0, b_batch=0, sfa_batch=0, c_batch=1000)),
+    (127, 16384, 3, 1, dict(a_batch=127 * 8192 + 4096, b_batch=64 * 8192, sfa_batch=4 * 131072 + 512,
+                            sfb_batch=131072 + 1024, c_batch=200)),
+    (7168, 2048, 4, 1, dict(b_batch=128 * 1024, c_batch=8192)),
+    (33, 8192, 2, 0, dict(a_row=4096 + 16, sfa_row=512 + 32, sfa_batch=33 * 544, c_batch=40)),
+]
+
+
+@pytest.mark.parametrize("M,K,L,layout,over", STRIDED)
+def test_kernel_addresses_in_bounds_strided(M, K, L, layout, over):
+    check_shape(M, K, L, layout, strides=strided(M, K, L, layout, **over))

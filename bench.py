@@ -105,6 +105,74 @@ def cpu_baseline(w, layout: str, budget_s: float):
             "us_per_call": round(sec_per_call * 1e6, 1)}
 
 
+def bench_small_n(args, w, dev):
+    """N-vector skinny GEMM on the workload's A: HBM bytes = A + SFA + N vectors
+    of B and SFB + the N float16 columns of C."""
+    import torch
+    import block_scaled_fp4_gemv_amd as g
+    M, K, L, N, layout = w.M, w.K, w.L, args.small_n, args.layout
+    sizes = g.small_n_operand_bytes(M, N, K, L, layout)
+    ideal = L * (M * K // 2 + M * K // 16 + N * (K // 2 + K // 16) + 2 * N * M)
+    per_set = sizes["a"] + sizes["sfa"]
+    nsets = max(1, min(64, -(-ROTATE_BYTES // per_set)))
+    log(f"small-N {w.name} N={N}: {nsets} sets of {per_set / 1e6:.1f} MB")
+    rng = np.random.default_rng([7, M, N, K, L])
+    b_codes = synth.pack_nibbles(rng.integers(0, 16, (L, N, K), dtype=np.uint8))
+    sfb_plain = synth.scale_codes(rng, (L, N, K // 16))
+    sfb_host = synth.to_blocked(sfb_plain, pad=0) if layout == "blocked" else sfb_plain
+    b_dev, sfb_dev = torch.from_numpy(b_codes).to(dev), torch.from_numpy(np.ascontiguousarray(sfb_host)).to(dev)
+    sets = []
+    for i in range(nsets):
+        inp = synth.make_inputs(w, i)
+        sets.append((torch.from_numpy(inp.a).to(dev), torch.from_numpy(inp.sfa(layout)).to(dev),
+                     torch.empty(L * N * M, dtype=torch.float16, device=dev)))
+        if i == 0:
+            inp0 = inp
+
+    def step(i, stream=None):
+        a, sfa, c = sets[i % nsets]
+        g.nvfp4_gemm_small_n(a, b_dev, sfa, sfb_dev, c, M, N, K, L, layout, 1.0, stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    verified = None
+    if not args.no_verify:
+        import oracle
+        oracle.build(force=False)
+        step(0)
+        torch.cuda.synchronize()
+        got = sets[0][2].cpu().view(torch.int16).numpy().view(np.uint16).reshape(L, N, M)
+        ref = oracle.gemm_small_n(inp0.a, b_codes, inp0.sfa_plain, sfb_plain, M, N, K, L,
+                                  nthreads=min(os.cpu_count() or 1, 16))
+        verified = bool(oracle.check(got, ref).all())
+        log(f"small-N parity vs oracle on set 0: {'ok' if verified else 'FAILED'}")
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(args.steps):
+            step(i, cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = ideal / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"µs/call and achieved HBM GB/s of the {N}-vector NVFP4 skinny GEMM",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"small_n{N}_{w.name}", "M": M, "N": N, "K": K, "L": L, "sf_layout": layout,
+                   "ideal_bytes_per_call": ideal, "plan": g.nvfp4_gemm_small_n_plan(M, N, K, L)},
+        "us_per_call": round(ms * 1e3, 3), "verified_vs_oracle": verified,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}), flush=True)
+
+
 def bench_reblock(args, w, dev):
     """Device reblock of the workload's plain SFA [L][M][K/16] into the 128x4
     blocked layout: HBM bytes = plain read + blocked write."""
@@ -182,6 +250,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--small-n", type=int, default=0, metavar="N",
+                    help="time the N-vector skinny GEMM (N = 1..8) on the workload's A instead "
+                         "(its own JSON line)")
     ap.add_argument("--reblock", action="store_true",
                     help="time the device plain -> blocked reblock of the workload's SFA instead "
                          "(its own JSON line)")
@@ -216,6 +287,9 @@ def main():
     w = WORKLOADS[args.workload]
     if args.reblock:
         bench_reblock(args, w, dev)
+        return
+    if args.small_n:
+        bench_small_n(args, w, dev)
         return
     layout = args.layout
     props = torch.cuda.get_device_properties(dev)

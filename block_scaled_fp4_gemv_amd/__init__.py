@@ -44,6 +44,8 @@ EXPORTED_SYMBOLS = (
     "nvfp4_gemv_strided",
     "nvfp4_gemv_dense_strides",
     "nvfp4_gemv_plan",
+    "nvfp4_gemm_small_n",
+    "nvfp4_gemm_small_n_plan",
     "nvfp4_scales_to_blocked",
     "nvfp4_blocked_scales_bytes",
     "nvfp4_status_string",
@@ -114,6 +116,11 @@ def lib():
     L.nvfp4_gemv_workspace_bytes.argtypes = [i64, i64, i64]
     L.nvfp4_gemv_plan.restype = i32
     L.nvfp4_gemv_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    L.nvfp4_gemm_small_n.restype = i32
+    L.nvfp4_gemm_small_n.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.c_float, vp]
+    L.nvfp4_gemm_small_n_plan.restype = i32
+    L.nvfp4_gemm_small_n_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]
     L.nvfp4_scales_to_blocked.restype = i32
     L.nvfp4_scales_to_blocked.argtypes = [vp, vp, i64, i64, i64, vp]
     L.nvfp4_blocked_scales_bytes.restype = ctypes.c_size_t
@@ -270,6 +277,40 @@ def nvfp4_gemv_plan(M: int, K: int, L: int) -> dict:
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemv_plan")
     return plan.as_dict()
+
+
+def nvfp4_gemm_small_n_plan(M: int, N: int, K: int, L: int) -> dict:
+    r, wg, lds = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+    st = lib().nvfp4_gemm_small_n_plan(M, N, K, L, ctypes.byref(r), ctypes.byref(wg), ctypes.byref(lds))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemm_small_n_plan")
+    return {"rows_per_wg": r.value, "workgroups": wg.value, "lds_bytes": lds.value}
+
+
+def small_n_operand_bytes(M: int, N: int, K: int, L: int, layout) -> dict:
+    """Bytes each operand of nvfp4_gemm_small_n must hold."""
+    lay = layout_id(layout)
+    nkb = K // 16
+    if lay == NVFP4_SF_BLOCKED:
+        sfa, sfb = L * cdiv(M, 128) * cdiv(nkb, 4) * 512, L * cdiv(N, 128) * cdiv(nkb, 4) * 512
+    else:
+        sfa, sfb = L * M * nkb, L * N * nkb
+    return {"a": L * M * K // 2, "b": L * N * K // 2, "sfa": sfa, "sfb": sfb, "c": 2 * L * N * M}
+
+
+def nvfp4_gemm_small_n(a, b, sfa, sfb, c, M: int, N: int, K: int, L: int, sf_layout,
+                       alpha: float = 1.0, stream=None) -> None:
+    """Enqueue c[l][n][m] = fp16(alpha * sum_k A*SFA*B_n*SFB_n) for N = 1..8 vectors."""
+    (pa, na), (pb, nb), (psa, nsa), (psb, nsb), (pc, nc) = map(_ptr_and_bytes, (a, b, sfa, sfb, c))
+    lay = layout_id(sf_layout)
+    if M >= 1 and K >= 32 and K % 32 == 0 and L >= 1 and 1 <= N <= 8:
+        need = small_n_operand_bytes(M, N, K, L, lay)
+        for name, nbytes in dict(a=na, b=nb, sfa=nsa, sfb=nsb, c=nc).items():
+            if nbytes is not None and nbytes < need[name]:
+                raise ValueError(f"{name} holds {nbytes} bytes, the shape needs {need[name]}")
+    st = lib().nvfp4_gemm_small_n(pa, pb, psa, psb, pc, M, N, K, L, lay, float(alpha), _stream_handle(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemm_small_n")
 
 
 def nvfp4_blocked_scales_bytes(rows: int, K: int, L: int) -> int:

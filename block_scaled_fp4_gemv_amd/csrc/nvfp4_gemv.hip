@@ -59,13 +59,9 @@
 
 #include "nvfp4_gemv.h"
 #include "nvfp4_internal.h"
+#include "nvfp4_device.h"
 
 namespace {
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;                 // compute waves per workgroup
 constexpr int kThreads = 64 * kWaves;     // compute threads
@@ -77,7 +73,6 @@ constexpr int kMaxLpr = 256;              // lanes per row, at most the compute 
 constexpr int kSfaLdsBudget = 48 * 1024;  // staged scale bytes per workgroup
 constexpr int kDmaBytes = 64 * 16;        // LDS bytes one wave-wide 16-byte direct-to-LDS load fills
 constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
-constexpr int kXcds = 8;                  // MI355X: 8 XCDs, WG ids dealt round-robin
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
 constexpr int kCachePolicyNT = 2;         // buffer load cache policy: non-temporal
@@ -108,14 +103,6 @@ struct Params {
     float *partials;      // [L*M][S] when S > 1
 };
 
-// Contiguous logical ids per XCD: hardware id i runs on XCD i % 8.
-__device__ inline uint32_t xcd_remap(uint32_t i, uint32_t n)
-{
-    const uint32_t x = i % kXcds, j = i / kXcds;
-    const uint32_t q = n / kXcds, r = n % kXcds;
-    return x * q + min(x, r) + j;
-}
-
 // Row of local row q of a workgroup whose first slot is first: slot
 // first + q/4, sub-row q%4 (the 32-row group inside the 128-row block).
 __device__ inline int32_t slot_row(int32_t first, int32_t q)
@@ -133,65 +120,10 @@ __device__ inline int64_t sf_pair_offset(int64_t r, int32_t c, int32_t nkb, int3
     return ((r >> 7) * ncb + (c >> 1)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 1) * 2;
 }
 
-// Reinterpretation helpers. They take their operand by value on purpose:
-// applying __builtin_bit_cast to an ext-vector element such as `v.y` directly
-// read the vector's first element with this compiler.
-__device__ __attribute__((always_inline)) inline half2_t as_h2(uint32_t v)
-{
-    return __builtin_bit_cast(half2_t, v);
-}
-__device__ __attribute__((always_inline)) inline uint32_t as_u32(half2_t v)
-{
-    return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __attribute__((always_inline)) inline float as_f32(int v)
-{
-    return __builtin_bit_cast(float, v);
-}
-__device__ __attribute__((always_inline)) inline int as_i32(float v)
-{
-    return __builtin_bit_cast(int, v);
-}
-
 // 16 bytes of A, streamed once: non-temporal
 __device__ __attribute__((always_inline)) inline uint4_t load_a(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNT);
-}
-
-// two E2M1 codes (byte SEL of w, low nibble first) -> two float16 values
-template <int SEL>
-__device__ __attribute__((always_inline)) inline half2_t fp4x2(uint32_t w)
-{
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-}
-
-// float32 -> float16 bits, round to nearest even, overflow to +-inf
-__device__ __attribute__((always_inline)) inline uint16_t f16_bits(float v)
-{
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-
-// Sum over aligned groups of RED lanes (RED = 1..64, a power of two) with DPP.
-// The group's sum ends in its last lane: row_shr accumulates a window of RED
-// lanes inside each 16-lane row, row_bcast15 / row_bcast31 carry the row sums
-// across rows.
-template <int RED>
-__device__ __attribute__((always_inline)) inline float group_sum(float v)
-{
-    if (RED >= 2)
-        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x111, 0xF, 0xF, true));  // row_shr:1
-    if (RED >= 4)
-        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x112, 0xF, 0xF, true));  // row_shr:2
-    if (RED >= 8)
-        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x114, 0xF, 0xF, true));  // row_shr:4
-    if (RED >= 16)
-        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x118, 0xF, 0xF, true));  // row_shr:8
-    if (RED >= 32)
-        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x142, 0xA, 0xF, false)); // row_bcast:15
-    if (RED >= 64)
-        v += as_f32(__builtin_amdgcn_update_dpp(0, as_i32(v), 0x143, 0xC, 0xF, false)); // row_bcast:31
-    return v;
 }
 
 // Sum over one 16-element scale block: dwords w0, w1 of A (8 codes each)
@@ -209,21 +141,6 @@ __device__ __attribute__((always_inline)) inline float dot_block(uint32_t w0, ui
     s = __builtin_amdgcn_fdot2(fp4x2<2>(w1), as_h2(b1.z), s, false);
     s = __builtin_amdgcn_fdot2(fp4x2<3>(w1), as_h2(b1.w), s, false);
     return s;
-}
-
-// b' of one chunk: 16 bytes of packed B (32 codes) times its two SFB scales.
-__device__ __attribute__((always_inline)) inline void make_bprime(uint4_t b, uint32_t sfb2,
-                                                                  uint4_t (&out)[4])
-{
-    const half2_t sf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sfb2, 1.0f, false);
-    const half2_t s0 = {sf.x, sf.x}, s1 = {sf.y, sf.y};
-    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const half2_t sc = d < 2 ? s0 : s1;
-        out[d] = {as_u32(fp4x2<0>(w[d]) * sc), as_u32(fp4x2<1>(w[d]) * sc),
-                  as_u32(fp4x2<2>(w[d]) * sc), as_u32(fp4x2<3>(w[d]) * sc)};
-    }
 }
 
 template <int LAYOUT, int LPR, bool SPLIT>

@@ -194,6 +194,34 @@ typedef struct {
 nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan);
 
 /*
+ * Block-scaled skinny GEMM with N = 1..8 right-hand vectors (the general
+ * product kernelbot NVFP4 GEMV submission 103289 hands to torch._scaled_mm,
+ * a @ b^T with block scales and a float16 result; the GEMV is N = 1):
+ *
+ *   c[l][n][m] = fp16( alpha * sum_{k<K} e2m1(A[l][m][k]) * e4m3(SFA[l][m][k/16])
+ *                                      * e2m1(B[l][n][k]) * e4m3(SFB[l][n][k/16]) )
+ *
+ *   a    uint8 [L][M][K/2]      as for nvfp4_gemv
+ *   b    uint8 [L][N][K/2]      N packed vectors per batch
+ *   sfa  as for nvfp4_gemv (layout sf_layout)
+ *   sfb  plain uint8 [L][N][K/16]; blocked: the 128x4 layout of the N x K/16
+ *        matrix (rows padded to 128), ceil(K/64)*512 bytes per batch
+ *   c    fp16 [L][N][M]          written (column n of batch l contiguous)
+ * Requirements and alignment as for nvfp4_gemv, 1 <= N <= 8, alpha finite.
+ * Accumulation is float32 per row and vector (summation order the library's
+ * own); no K-split and no workspace: small M*L leaves the GPU partly idle.
+ */
+nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa, const void *sfb,
+                                  void *c, int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout,
+                                  float alpha, void *stream);
+
+/* Launch plan of nvfp4_gemm_small_n for a shape: rows per workgroup,
+ * workgroups (256 threads each) and dynamic LDS bytes; any output pointer may
+ * be NULL. Returns NVFP4_ERR_INVALID_SHAPE for shapes it does not take. */
+nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t L, int32_t *rows_per_wg,
+                                       int64_t *workgroups, int32_t *lds_bytes);
+
+/*
  * Device-side reblocking of plain scale factors into the 128x4 blocked layout
  * (the transformation kernelbot NVFP4 GEMV submission 69953 performs with
  * `to_blocked_batch` and submission 69575 with `blocked_transform_kernel`,

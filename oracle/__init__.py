@@ -121,6 +121,18 @@ def sf_batch_bytes(layout: int, rows: int, nkb: int) -> int:
     return _load().nvo_sf_batch_bytes(layout, rows, nkb)
 
 
+def gemm_small_n(a, b, sfa, sfb, M: int, N: int, K: int, L: int, nthreads: int = 0,
+                 alpha: float = 1.0) -> Result:
+    """Oracle of the N-vector skinny GEMM: column n is the GEMV of A against
+    vector n. a [L][M][K/2], b [L][N][K/2], plain scales sfa [L][M][K/16],
+    sfb [L][N][K/16]. Arrays of the result are [L][N][M]."""
+    b = np.asarray(b, np.uint8).reshape(L, N, K // 2)
+    sfb = np.asarray(sfb, np.uint8).reshape(L, N, K // 16)
+    cols = [gemv_arrays(a, b[:, n], sfa, sfb[:, n], M, K, L, PLAIN, nthreads, alpha) for n in range(N)]
+    st = lambda f: np.stack([getattr(r, f) for r in cols], axis=1)
+    return Result(st("c"), st("s_f64"), st("s_abs"), st("s_exact"), st("nan"), _alpha32(alpha))
+
+
 def reblock(plain, rows: int, K: int, L: int) -> np.ndarray:
     """Plain scales [L][rows][K/16] -> blocked bytes [L][per-batch bytes],
     padding 0 (the oracle of the device reblock)."""

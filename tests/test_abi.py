@@ -248,3 +248,25 @@ def test_strided_cases_pass_validation():
         st = strided_call(layout, M, K, L, **over)
         assert st not in (g.NVFP4_ERR_INVALID_STRIDE, g.NVFP4_ERR_INVALID_SHAPE, g.NVFP4_ERR_MISALIGNED), \
             (M, K, L, layout, over)
+
+
+def test_small_n_validation():
+    lib = g.lib()
+    base = (OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"], OK_ARGS["c"])
+    assert lib.nvfp4_gemm_small_n(*base, 128, 0, 256, 1, 0, 1.0, None) == g.NVFP4_ERR_INVALID_SHAPE
+    assert lib.nvfp4_gemm_small_n(*base, 128, 9, 256, 1, 0, 1.0, None) == g.NVFP4_ERR_INVALID_SHAPE
+    assert lib.nvfp4_gemm_small_n(*base, 128, 2, 48, 1, 0, 1.0, None) == g.NVFP4_ERR_INVALID_SHAPE
+    assert lib.nvfp4_gemm_small_n(*base, 128, 2, 256, 1, 5, 1.0, None) == g.NVFP4_ERR_INVALID_LAYOUT
+    assert lib.nvfp4_gemm_small_n(*base, 128, 2, 256, 1, 0, float("nan"), None) == g.NVFP4_ERR_INVALID_SCALE
+    bad = (OK_ARGS["a"] + 8,) + base[1:]
+    assert lib.nvfp4_gemm_small_n(*bad, 128, 2, 256, 1, 0, 1.0, None) == g.NVFP4_ERR_MISALIGNED
+    assert lib.nvfp4_gemm_small_n(None, *base[1:], 128, 2, 256, 1, 0, 1.0, None) == g.NVFP4_ERR_NULL_POINTER
+
+
+def test_small_n_plan():
+    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1)
+    assert p["workgroups"] == 256 and p["rows_per_wg"] == 28
+    p = g.nvfp4_gemm_small_n_plan(100000, 8, 64, 1)
+    assert p["lds_bytes"] <= 48 * 1024
+    with pytest.raises(g.Nvfp4Error):
+        g.nvfp4_gemm_small_n_plan(128, 9, 256, 1)

@@ -1,0 +1,83 @@
+"""GPU parity of the N-vector skinny GEMM (nvfp4_gemm_small_n) against the
+oracle (N independent GEMVs), within the GEMV's tolerance per output; plain
+and blocked scales give bit-identical results; the global scale applies;
+outputs outside c are untouched."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_gemv_amd as g  # noqa: E402
+from gpu_util import to_dev  # noqa: E402
+from test_oracle_small_n import inputs  # noqa: E402
+
+TAIL = 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle_built():
+    oracle.build(force=False)
+
+
+def blocked_rows(plain):
+    """Plain scales [L][rows][K/16] -> blocked bytes [L][per batch] (synth's view chain)."""
+    return synth.to_blocked(plain, pad=0)
+
+
+def run_small_n(a, b, sfa, sfb, M, N, K, L, layout, alpha=1.0):
+    c = torch.full((L * N * M + TAIL,), -1, dtype=torch.int16, device="cuda").view(torch.float16)
+    if layout == "blocked":
+        sfa, sfb = blocked_rows(sfa), blocked_rows(sfb)
+    g.nvfp4_gemm_small_n(to_dev(a), to_dev(b), to_dev(sfa), to_dev(sfb), c[:L * N * M], M, N, K, L, layout, alpha)
+    torch.cuda.synchronize()
+    bits = c.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.all(bits[L * N * M:] == 0xFFFF), "write past the end of c"
+    return bits[:L * N * M].reshape(L, N, M)
+
+
+CASES = [(1, 1, 32, 1), (7, 3, 96, 2), (128, 2, 2048, 1), (300, 4, 20480, 2), (1000, 8, 4096, 3),
+         (7168, 8, 2048, 1), (129, 5, 16384, 1), (4096, 2, 7168, 2), (64, 7, 65536, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,L", CASES)
+def test_small_n_parity(M, N, K, L):
+    a, b, sfa, sfb = inputs(M, N, K, L, M + N + K)
+    ref = oracle.gemm_small_n(a, b, sfa, sfb, M, N, K, L)
+    outs = {}
+    for layout in ("plain", "blocked"):
+        got = run_small_n(a, b, sfa, sfb, M, N, K, L, layout)
+        rep = oracle.check_report(got, ref)
+        assert rep == "", f"{layout}\n{rep}"
+        outs[layout] = got
+    assert np.array_equal(outs["plain"], outs["blocked"])
+
+
+def test_small_n_alpha_and_edge_codes():
+    M, N, K, L = 1000, 4, 4096, 2
+    inp = [synth.random_inputs(M, K, L, seed=60 + n, dist="edge") for n in range(N)]
+    a = inp[0].a
+    b = np.stack([x.b.reshape(L, K // 2) for x in inp], axis=1)
+    sfa = inp[0].sfa_plain
+    sfb = np.stack([x.sfb_plain for x in inp], axis=1)
+    for alpha in (1.0, -0.375):
+        ref = oracle.gemm_small_n(a, b, sfa, sfb, M, N, K, L, alpha=alpha)
+        got = run_small_n(a, b, sfa, sfb, M, N, K, L, "blocked", alpha)
+        assert oracle.check_report(got, ref) == ""
+
+
+def test_small_n_headline_shape():
+    M, N, K, L = 7168, 8, 16384, 1
+    a, b, sfa, sfb = inputs(M, N, K, L, 5)
+    got = run_small_n(a, b, sfa, sfb, M, N, K, L, "blocked")
+    rows = np.arange(0, M, 97)
+    for n in (0, 7):
+        ref = oracle.gemm_small_n(a[:, rows], b[:, n:n + 1], sfa[:, rows], sfb[:, n:n + 1], rows.size, 1, K, L)
+        col = oracle.Result(ref.c[:, 0], ref.s_f64[:, 0], ref.s_abs[:, 0], ref.s_exact[:, 0], ref.nan[:, 0])
+        assert oracle.check(got[:, n, rows], col).all()

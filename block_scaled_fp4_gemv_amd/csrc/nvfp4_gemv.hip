@@ -17,9 +17,9 @@
 // read once into LDS; plain scales are staged from their rows. Both layouts
 // then run the same arithmetic and give bit-identical results.
 //
-// Roles. Four waves compute; a fifth stages the scales of the workgroup's
-// rows into LDS with direct-to-LDS loads (global_load_lds), all in flight at
-// once. A wave's vector loads complete in order, so scale loads issued by a
+// Roles. Four waves compute; a fifth (wave 0, the first one launched) stages
+// the scales of the workgroup's rows into LDS with direct-to-LDS loads
+// (global_load_lds), all in flight at once. A wave's vector loads complete in order, so scale loads issued by a
 // computing wave would hold back every later A load of that wave; from a wave
 // of their own they stream beside A. The computing waves start on A at once:
 // the first rounds keep their exact block sums and take the scales after the
@@ -65,7 +65,7 @@ namespace {
 
 constexpr int kWaves = 4;                 // compute waves per workgroup
 constexpr int kThreads = 64 * kWaves;     // compute threads
-constexpr int kBlock = kThreads + 64;     // plus one wave that stages the scales
+constexpr int kBlock = kThreads + 64;     // plus one wave (wave 0) that stages the scales
 constexpr int kCpl = 4;                   // chunks per lane per K-segment
 constexpr int kPrefetch = 8;              // chunk loads in flight per lane (multiple of kCpl)
 constexpr int kDeferRounds = 2;           // first row rounds that keep block sums (multiple of the ring's rounds)
@@ -173,14 +173,16 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const int32_t c_begin = s * p.kc_split;
     const int32_t c_end = min(c_begin + p.kc_split, nchunks);
 
-    // Threads 0 .. kThreads-1 compute; the last wave only stages the scales.
+    // One wave stages the scales, the others compute.
     // A wave's vector loads complete in order, so scale loads issued by a
     // computing wave would hold back every later A load of that wave; issued
     // by a wave of their own, they stream beside the A loads.
-    const int tid = threadIdx.x;
-    // wave-uniform (scalar) so that the two roles are separate paths, not
-    // one path with two lane masks whose registers would all be live at once
-    const bool loader = __builtin_amdgcn_readfirstlane(tid) >= kThreads;
+    // Wave 0 stages the scales (it is launched first), waves 1..4 compute.
+    // The role is wave-uniform (scalar) so that the two roles are separate
+    // paths, not one path with two lane masks whose registers would all be
+    // live at once.
+    const bool loader = __builtin_amdgcn_readfirstlane((int)threadIdx.x) < 64;
+    const int tid = loader ? (int)threadIdx.x : (int)threadIdx.x - 64;
     const int grp = tid / LPR, j = tid % LPR;
     const int lane = tid & 63;
     const int wig = WPG > 1 ? j >> 6 : 0;                 // wave index inside the row group

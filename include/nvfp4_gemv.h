@@ -177,7 +177,7 @@ nvfp4_status_t nvfp4_gemv_strided(const void *a, const void *b, const void *sfa,
  *   rows_per_wg    output rows per workgroup (at most; 4 per 16-byte scale slot)
  *   k_splits       number of K-slices (1 = no split)
  *   k_per_split    K-elements per slice
- *   workgroups     grid size; threads_per_wg threads each (the last 64 of
+ *   workgroups     grid size; threads_per_wg threads each (the first 64 of
  *                  them stage the scales, the others compute)
  *   lds_bytes      dynamic LDS per workgroup
  */

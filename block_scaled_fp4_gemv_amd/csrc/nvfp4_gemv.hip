@@ -70,8 +70,9 @@ constexpr int kCpl = 4;                   // chunks per lane per K-segment
 constexpr int kPrefetch = 8;              // chunk loads in flight per lane (multiple of kCpl)
 constexpr int kDeferRounds = 2;           // first row rounds that keep block sums (multiple of the ring's rounds)
 constexpr int kMaxLpr = 256;              // lanes per row, at most the compute threads
-constexpr int kSfaLdsBudget = 48 * 1024;  // staged scale bytes per workgroup
+constexpr int kSfaLdsBudget = 36 * 1024;  // staged SFA bytes per workgroup (B, SFB and sums fit in 64 KiB)
 constexpr int kDmaBytes = 64 * 16;        // LDS bytes one wave-wide 16-byte direct-to-LDS load fills
+constexpr bool kStageB = true;            // blocked layout: B is staged with SFB (else the computing waves load it)
 constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
@@ -143,6 +144,37 @@ __device__ __attribute__((always_inline)) inline float dot_block(uint32_t w0, ui
     return s;
 }
 
+// s_waitcnt vmcnt(k) for a wave-uniform k (the count is an immediate; k
+// above 63, the counter's limit, waits as 63 does)
+template <int K0 = 0>
+__device__ __attribute__((always_inline)) inline void wait_vmcnt(int k)
+{
+    if constexpr (K0 < 63) {
+        if (k == K0) {
+            __builtin_amdgcn_s_waitcnt((kWaitVmcnt0 & ~0xC00F) | (K0 & 15) | ((K0 >> 4) << 14));
+            return;
+        }
+        wait_vmcnt<K0 + 1>(k);
+    } else {
+        __builtin_amdgcn_s_waitcnt((kWaitVmcnt0 & ~0xC00F) | 15 | (3 << 14));
+    }
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_dst + lane*16
+// (global_load_lds_dwordx4, LDS address from M0). Inline assembly so that the
+// compiler does not track the copy: the staging wave orders its copies with
+// its own vmcnt waits, and the compiler would otherwise wait for all of them
+// before the first barrier. Nothing else in this file uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __attribute__((always_inline)) inline void copy16_to_lds(const void *src, const uint8_t *lds_dst)
+{
+    const uint32_t addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int LAYOUT, int LPR, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
@@ -193,8 +225,18 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
     const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
     const uint8_t *b_l = B + (int64_t)l * p.b_batch;
-    uint8_t *stage = lds;                                  // staged scales of the segment
-    float *part = (float *)(lds + p.stage_bytes);          // [nq][WPG] per-wave row sums
+    // Blocked layout: the staging wave stages b's inputs too, the 16-byte SFB
+    // lines that hold row 0 (the scale pairs the lanes need sit 512 bytes
+    // apart: one scattered 2-byte read each) and B. Plain: the computing waves
+    // load them (one contiguous run each). The LDS areas are reserved either way.
+    constexpr bool STAGE_SFB = LAYOUT == NVFP4_SF_BLOCKED;
+    constexpr bool STAGE_B = STAGE_SFB && kStageB;
+    constexpr int BSTB = kStageB ? (64 * LPR + kDmaBytes - 1) / kDmaBytes * kDmaBytes : 0;   // staged B bytes
+    constexpr int SFBB = (32 * LPR + kDmaBytes - 1) / kDmaBytes * kDmaBytes;   // staged blocked SFB bytes
+    uint8_t *stage = lds;                                  // staged SFA of the segment
+    uint8_t *b_stage = lds + p.stage_bytes;                // staged B of the segment: chunk c at c*16
+    uint8_t *sfb_stage = b_stage + BSTB;                   // staged blocked SFB: 4-block group g at g*16
+    float *part = (float *)(sfb_stage + SFBB);             // [nq][WPG] per-wave row sums
 
     // A through a buffer resource based at the first row of this workgroup's
     // first 128-row block: 32-bit lane offsets (the rows of one workgroup lie
@@ -212,18 +254,30 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     // = 16 bytes at (cb * nslots + sl) * 16, i.e. row 4 sl + i4 at +4 i4 and
     // chunk c of the group (2 scales) at +2 (c & 1); plain: the 2 scales of
     // (row q, chunk c) at (q * nck + c) * 2. Both roles pass the same barriers:
-    // per segment one after the previous segment's scales are read (not before
-    // the first) and one that publishes the staged scales; then the ones of
-    // the epilogue.
+    // per segment one after the previous segment's staged bytes are read (not
+    // before the first), (blocked) one after b's inputs are staged and one
+    // that publishes the staged scales of A; then the ones of the epilogue.
     if (loader) {
         // raised issue priority: its copies gate the publish barrier, and the
         // computing waves' A loads would otherwise take every free issue slot
         __builtin_amdgcn_s_setprio(3);
+        // nothing is in flight yet; saying so keeps the compiler from waiting
+        // on the copies (it cannot see them) inside the issue loops below
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         for (int32_t c0 = c_begin; c0 < c_end; c0 += SEG) {
             const int32_t nck = min(SEG, c_end - c0);
             if (c0 != c_begin)
-                __syncthreads();                           // the previous segment's scales are read
+                __syncthreads();                           // the previous segment's staged bytes are read
             const int32_t ncb_seg = (nck + 1) >> 1, cb0 = c0 >> 1, units = nck >> 3;
+            // b's inputs go first: b' waits for them, the scales of A only
+            // for the deferred rounds' end. Past the end the index clamps.
+            const int32_t nbc = STAGE_B ? (nck + 63) >> 6 : 0;
+            const int32_t nsfb = STAGE_SFB ? (ncb_seg + 63) >> 6 : 0;
+            for (int32_t i = 0; i < nbc; ++i)
+                copy16_to_lds(b_l + (int64_t)(c0 + min(i * 64 + lane, nck - 1)) * 16, b_stage + i * kDmaBytes);
+            for (int32_t i = 0; i < nsfb; ++i)
+                copy16_to_lds(sfb_l + (int64_t)(cb0 + min(i * 64 + lane, ncb_seg - 1)) * 512,
+                              sfb_stage + i * kDmaBytes);
             if (!direct) {
                 // Wave-wide direct-to-LDS load i puts item i*64 + lane at
                 // (i*64 + lane) * 16; all loads are in flight at once. Item it
@@ -248,9 +302,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                         const int32_t r = min(slot_row(first, mjc), M - 1);
                         src = sfa_l + (int64_t)r * p.sfa_row + 2 * c0 + 16 * mn;
                     }
-                    __builtin_amdgcn_global_load_lds((const void *)src,
-                                                     (__attribute__((address_space(3))) void *)(stage + i * kDmaBytes),
-                                                     16, 0, 0);
+                    copy16_to_lds(src, stage + i * kDmaBytes);
                     mn += dmin;
                     mj += dmaj;
                     if (mn >= per) {
@@ -258,7 +310,11 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                         ++mj;
                     }
                 }
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the staged bytes are in LDS
+                if (STAGE_SFB) {
+                    wait_vmcnt(nload);                     // the copies of b's inputs have landed
+                    __syncthreads();                       // b' inputs are staged
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the staged scales are in LDS
             } else {
                 // plain scales whose rows are not 16-byte multiples: 2 bytes at a time
                 for (int32_t it = lane; it < nq * nck; it += 64) {
@@ -281,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         const int32_t nck = min(SEG, c_end - c0);
         const bool first_seg = c0 == c_begin;
         if (!first_seg)
-            __syncthreads();                               // the previous segment's scales are read
+            __syncthreads();                               // the previous segment's staged bytes are read
 
         auto row_off = [&](int32_t n) -> uint32_t {
             const int32_t q = min(grp + G * n, nq - 1);
@@ -371,8 +427,8 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 store_row(grp + G * n, acc);
         };
 
-        // ---- the first kPrefetch steps of A, then B and SFB for b' (A first:
-        // b' waits for all of them anyway, and the stream starts sooner)
+        // ---- the first kPrefetch steps of A, then b' (A first: the stream
+        // starts sooner, and b' waits for its inputs anyway)
 #pragma unroll
         for (int u = 0; u < kPrefetch; ++u)
             abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
@@ -382,10 +438,22 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
 #pragma unroll
         for (int k = 0; k < kCpl; ++k) {
             const int32_t ci = c0 + min(j + k * LPR, nck - 1);
-            bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
-            sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
+            if (!STAGE_B)
+                bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
+            if (!STAGE_SFB)
+                sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (STAGE_SFB) {
+            __syncthreads();                               // b' inputs are staged
+#pragma unroll
+            for (int k = 0; k < kCpl; ++k) {
+                const int32_t cc = min(j + k * LPR, nck - 1);
+                if (STAGE_B)
+                    bload[k] = *(const uint4_t *)(b_stage + cc * 16);
+                sload[k] = *(const uint16_t *)(sfb_stage + (cc >> 1) * 16 + (cc & 1) * 2);
+            }
+        }
         // b' for this lane's chunks of the segment (registers, reused for every row)
 #pragma unroll
         for (int k = 0; k < kCpl; ++k)
@@ -593,7 +661,9 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
     pl.n_wg = (int64_t)pl.P * L * S;
     const int wpg = pl.lpr > 64 ? pl.lpr / 64 : 1;
     pl.stage_bytes = stage_bytes(pl.lpr, spw);
-    pl.lds_bytes = (int)(pl.stage_bytes + 4 * spw * wpg * (int)sizeof(float));
+    // staged SFA, staged B, staged blocked SFB, per-wave row sums
+    pl.lds_bytes = (int)(pl.stage_bytes + (kStageB ? align_up((size_t)(64 * pl.lpr), kDmaBytes) : 0) +
+                         align_up((size_t)(32 * pl.lpr), kDmaBytes) + 4 * spw * wpg * (int)sizeof(float));
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
     if (S > 1) {
         pl.ws_partials = align_up((size_t)(L * M * S) * sizeof(float), kWsAlign);

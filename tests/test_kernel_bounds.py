@@ -4,10 +4,11 @@ This mirrors the index arithmetic of nvfp4_gemv.hip for the whole grid of each
 tested shape, using the launch plan the library reports, and checks:
   * every A, B, SFA and SFB read is inside its buffer (A through a buffer
     resource: inside the resource's byte range),
-  * the staging wave's LDS writes stay inside the staging area, no two of them
-    hit one byte, and the scales the computing waves read for every real
-    (row, chunk) are exactly the ones staged there, byte for byte; no real row
-    reads padding of the blocked layout,
+  * the staging wave's LDS writes stay inside their areas (scales of A, B,
+    blocked SFB), no two of them hit one byte, and what the computing waves
+    read there (the scales of every real (row, chunk), each lane's B chunks
+    and their SFB scales) is exactly what was staged, byte for byte; no real
+    row reads padding of the blocked layout,
   * every output row is written exactly once, and split-K partial and ticket
     indices stay inside the workspace.
 Keep it in step with the kernel's constants: 4 computing waves and one staging
@@ -22,6 +23,7 @@ import synth
 THREADS, CPL, PREFETCH, XCDS, MAX_TICKETS = 256, 4, 8, 8, 1024
 LOADER = 64                 # threads of the staging wave
 DMA_BYTES = 64 * 16         # LDS bytes one wave-wide staging load fills
+STAGE_B = True              # blocked layout: the staging wave stages B as well as SFB
 
 
 def cdiv(a, b):
@@ -68,7 +70,9 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     assert n_wg == P * L * S
     SEG, G, WPG = lpr * CPL, THREADS // lpr, max(1, lpr // 64)
     stb = stage_bytes(lpr, spw)
-    assert lds_bytes == stb + 4 * spw * WPG * 4
+    bstb = cdiv(64 * lpr, DMA_BYTES) * DMA_BYTES if STAGE_B else 0
+    sfbb = cdiv(32 * lpr, DMA_BYTES) * DMA_BYTES
+    assert lds_bytes == stb + bstb + sfbb + 4 * spw * WPG * 4
     assert lds_bytes <= 64 * 1024
     sd = strides or g.nvfp4_gemv_dense_strides(M, K, L, layout)
     a_row, a_bat, b_bat, c_bat = sd["a_row"], sd["a_batch"], sd["b_batch"], sd["c_batch"]
@@ -107,7 +111,7 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
         nslots = min(spw, ns - first)
         assert nslots >= 1
         nq = 4 * nslots
-        assert stb + nq * WPG * 4 <= lds_bytes
+        assert stb + bstb + sfbb + nq * WPG * 4 <= lds_bytes
         c_begin, c_end = s * kc, min(s * kc + kc, nchunks)
         assert c_end > c_begin
         row_base = (first >> 5) << 7
@@ -164,14 +168,44 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                 assert (2 * it + 2).max() <= stb
                 lds_src[2 * it] = src
                 lds_src[2 * it + 1] = src + 1
-            # ---- b': B chunk and its two SFB scales
+            # ---- b' inputs staged by the staging wave (blocked layout): B
+            # chunks, then the 16-byte line of each 4-block SFB group that holds row 0
+            stage_b = layout == 1 and STAGE_B
+            b_src = np.full(bstb, -1, np.int64)
+            for i in range(cdiv(nck, 64) if stage_b else 0):
+                src = l * b_bat + (c0 + np.minimum(i * 64 + lane, nck - 1)) * 16
+                assert src.min() >= 0 and (src + 16).max() <= b_size and (src % 16 == 0).all()
+                dst = i * DMA_BYTES + lane * 16
+                assert (dst + 16).max() <= bstb, "staged B outside its area"
+                for b in range(16):
+                    b_src[dst + b] = src + b
+            sfb_src = np.full(sfbb, -1, np.int64)
+            if layout == 1:
+                for i in range(cdiv(ncb_seg, 64)):
+                    src = l * sfb_bat + (cb0 + np.minimum(i * 64 + lane, ncb_seg - 1)) * 512
+                    assert src.min() >= 0 and (src + 16).max() <= sfb_size and (src % 16 == 0).all()
+                    dst = i * DMA_BYTES + lane * 16
+                    assert (dst + 16).max() <= sfbb, "staged SFB outside its area"
+                    for b in range(16):
+                        sfb_src[dst + b] = src + b
+            # ---- b': each lane's B chunk and its two SFB scales
             for k in range(CPL):
-                ci = c0 + np.minimum(j + k * lpr, nck - 1)
-                boff = l * b_bat + ci * 16
-                assert boff.min() >= 0 and (boff + 16).max() <= b_size and (boff % 16 == 0).all()
+                cc = np.minimum(j + k * lpr, nck - 1)
+                ci = c0 + cc
+                if stage_b:
+                    for b in range(16):
+                        assert np.array_equal(b_src[cc * 16 + b], l * b_bat + ci * 16 + b), "staged B mismatch"
+                else:
+                    boff = l * b_bat + ci * 16
+                    assert boff.min() >= 0 and (boff + 16).max() <= b_size and (boff % 16 == 0).all()
                 so = sf_offset(layout, np.zeros_like(ci), 2 * ci, nkb, ncb)
                 assert (so + 1).max() < sfb_batch and (l * sfb_bat + so + 2).max() <= sfb_size
                 assert valid_sfb[so].all() and valid_sfb[so + 1].all()
+                if layout == 1:
+                    at = (cc >> 1) * 16 + (cc & 1) * 2
+                    assert (at + 2).max() <= sfbb
+                    assert np.array_equal(sfb_src[at], l * sfb_bat + so), "staged SFB mismatch"
+                    assert np.array_equal(sfb_src[at + 1], l * sfb_bat + so + 1), "staged SFB mismatch"
 
             # ---- computing waves: lane j reads, for its chunk k and round row q,
             # the 2 bytes at sfoff(c) + rowpart(q) (c, q clamped as in the kernel)

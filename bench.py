@@ -52,8 +52,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    src = os.path.join(ROOT, "block_scaled_fp4_gemv_amd", "csrc", "nvfp4_gemv.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """sha256 prefix of the GEMV kernel's sources (the kernel file, then its device header)."""
+    h = hashlib.sha256()
+    for f in ("nvfp4_gemv.hip", "nvfp4_device.h"):
+        h.update(open(os.path.join(ROOT, "block_scaled_fp4_gemv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(workload_name: str, layout: str):

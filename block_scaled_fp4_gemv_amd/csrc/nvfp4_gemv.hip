@@ -73,6 +73,7 @@ constexpr int kMaxLpr = 256;              // lanes per row, at most the compute 
 constexpr int kSfaLdsBudget = 36 * 1024;  // staged SFA bytes per workgroup (B, SFB and sums fit in 64 KiB)
 constexpr int kDmaBytes = 64 * 16;        // LDS bytes one wave-wide 16-byte direct-to-LDS load fills
 constexpr bool kStageB = true;            // blocked layout: B is staged with SFB (else the computing waves load it)
+constexpr int kSfaAhead = 20;             // blocked: A-scale copies issued before the wait for b's inputs
 constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
@@ -292,27 +293,38 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 const int32_t nload = (per * nmajor + 63) >> 6;
                 const int32_t dmaj = 64 / per, dmin = 64 % per;
                 int32_t mn = lane % per, mj = lane / per;
-                for (int32_t i = 0; i < nload; ++i) {
-                    const int32_t mjc = min(mj, nmajor - 1);
-                    const uint8_t *src;
-                    if (LAYOUT == NVFP4_SF_BLOCKED) {
-                        const int32_t sg = first + mn;
-                        src = sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + mjc) * 512 + (sg & 31) * 16;
-                    } else {
-                        const int32_t r = min(slot_row(first, mjc), M - 1);
-                        src = sfa_l + (int64_t)r * p.sfa_row + 2 * c0 + 16 * mn;
+                auto issue = [&](int32_t i0, int32_t i1) {
+                    for (int32_t i = i0; i < i1; ++i) {
+                        const int32_t mjc = min(mj, nmajor - 1);
+                        const uint8_t *src;
+                        if (LAYOUT == NVFP4_SF_BLOCKED) {
+                            const int32_t sg = first + mn;
+                            src = sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + mjc) * 512 + (sg & 31) * 16;
+                        } else {
+                            const int32_t r = min(slot_row(first, mjc), M - 1);
+                            src = sfa_l + (int64_t)r * p.sfa_row + 2 * c0 + 16 * mn;
+                        }
+                        copy16_to_lds(src, stage + i * kDmaBytes);
+                        mn += dmin;
+                        mj += dmaj;
+                        if (mn >= per) {
+                            mn -= per;
+                            ++mj;
+                        }
                     }
-                    copy16_to_lds(src, stage + i * kDmaBytes);
-                    mn += dmin;
-                    mj += dmaj;
-                    if (mn >= per) {
-                        mn -= per;
-                        ++mj;
-                    }
-                }
+                };
                 if (STAGE_SFB) {
-                    wait_vmcnt(nload);                     // the copies of b's inputs have landed
+                    // A CU holds only so many loads in flight; issuing every
+                    // copy before the wait would hold the computing waves at
+                    // the b' barrier until the last one is issued. So: some
+                    // copies, the wait for b's inputs, the barrier, the rest.
+                    const int32_t na = min(nload, kSfaAhead);
+                    issue(0, na);
+                    wait_vmcnt(na);                        // the copies of b's inputs have landed
                     __syncthreads();                       // b' inputs are staged
+                    issue(na, nload);
+                } else {
+                    issue(0, nload);
                 }
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the staged scales are in LDS
             } else {

@@ -10,6 +10,9 @@ distinct sets (>= 512 MiB together) that neither the L2s nor the 256 MiB
 Infinity Cache hold the next step's operands.
 
 Timing:
+  * parity of input set 0 against the oracle comes first; then W warmup
+    steps (whole replays of the K-step graph, back to back, so the clocks are
+    at their steady state under load when timing starts);
   * timed region: exactly K steps captured in one HIP graph (so host launch
     overhead is not measured), replayed once between two synchronisations;
     GPU time from events around the replay gives ms_per_step and ``value``.
@@ -108,6 +111,30 @@ def cpu_baseline(w, layout: str, budget_s: float):
             "us_per_call": round(sec_per_call * 1e6, 1)}
 
 
+def timed_graph(step, steps: int, warmup: int):
+    """Capture ``steps`` calls of ``step(i, stream)`` in one HIP graph, replay it
+    back to back until at least ``warmup`` untimed steps have run (the clocks
+    reach their steady state under load), then time exactly one replay between
+    two synchronisations. Returns (ms per step, warmup steps run)."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(steps):
+            step(i, cap)
+    torch.cuda.synchronize()
+    reps = max(1, -(-warmup // steps))
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, reps * steps
+
+
 def bench_small_n(args, w, dev):
     """N-vector skinny GEMM on the workload's A: HBM bytes = A + SFA + N vectors
     of B and SFB + the N float16 columns of C."""
@@ -135,8 +162,7 @@ def bench_small_n(args, w, dev):
     def step(i, stream=None):
         a, sfa, c = sets[i % nsets]
         g.nvfp4_gemm_small_n(a, b_dev, sfa, sfb_dev, c, M, N, K, L, layout, 1.0, stream)
-    for i in range(args.warmup):
-        step(i)
+    step(0)
     torch.cuda.synchronize()
     verified = None
     if not args.no_verify:
@@ -149,24 +175,11 @@ def bench_small_n(args, w, dev):
                                   nthreads=min(os.cpu_count() or 1, 16))
         verified = bool(oracle.check(got, ref).all())
         log(f"small-N parity vs oracle on set 0: {'ok' if verified else 'FAILED'}")
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.graph(graph, stream=cap):
-        for i in range(args.steps):
-            step(i, cap)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, warm = timed_graph(step, args.steps, args.warmup)
     gbs = ideal / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": f"µs/call and achieved HBM GB/s of the {N}-vector NVFP4 skinny GEMM",
-        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": warm,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"small_n{N}_{w.name}", "M": M, "N": N, "K": K, "L": L, "sf_layout": layout,
@@ -190,9 +203,6 @@ def bench_reblock(args, w, dev):
     for i in range(nsets):
         plains.append(torch.from_numpy(synth.make_inputs(w, i).sfa_plain).to(dev))
         outs.append(torch.empty(out_bytes, dtype=torch.uint8, device=dev))
-    for i in range(args.warmup):
-        g.nvfp4_scales_to_blocked(plains[i % nsets], outs[i % nsets], M, K, L)
-    torch.cuda.synchronize()
     verified = None
     if not args.no_verify:
         import oracle
@@ -202,24 +212,13 @@ def bench_reblock(args, w, dev):
         want = oracle.reblock(plains[0].cpu().numpy(), M, K, L).reshape(-1)
         verified = bool(np.array_equal(outs[0].cpu().numpy(), want))
         log(f"reblock parity vs oracle: {'ok' if verified else 'FAILED'}")
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.graph(graph, stream=cap):
-        for i in range(args.steps):
-            g.nvfp4_scales_to_blocked(plains[i % nsets], outs[i % nsets], M, K, L, cap)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    def rstep(i, stream=None):
+        g.nvfp4_scales_to_blocked(plains[i % nsets], outs[i % nsets], M, K, L, stream)
+    ms, warm = timed_graph(rstep, args.steps, args.warmup)
     gbs = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
     out = {"metric": "µs/call and achieved HBM GB/s of the plain -> 128x4 blocked SFA reblock",
            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+           "warmup": warm, "ms_per_step": round(ms, 6), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
            "config": {"workload": f"reblock_sfa_{w.name}", "rows": M, "K": K, "L": L,
                       "plain_bytes": in_bytes, "blocked_bytes": out_bytes, "rotating_sets": nsets},
@@ -247,7 +246,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps before the timed region (whole replays of the K-step graph)")
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
     ap.add_argument("--layout", default="blocked", choices=["blocked", "plain"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
@@ -320,44 +320,28 @@ def main():
         s = sets[i % nsets]
         g.nvfp4_gemv(s["a"], s["b"], s["sfa"], s["sfb"], s["c"], M, K, L, layout, stream)
 
-    # ---- warmup (also allocates any split-K workspace before graph capture)
-    for i in range(args.warmup):
-        step(i)
+    # ---- one call first (allocates any split-K workspace before graph capture)
+    step(0)
     torch.cuda.synchronize()
 
-    # ---- correctness of the benchmarked configuration (set 0) against the oracle
+    # ---- correctness of the benchmarked configuration (set 0) against the
+    # oracle, before the warmup so the GPU is not left idle before timing
     verified = None
     if not args.no_verify:
         import oracle
         oracle.build(force=False)
-        step(0)
-        torch.cuda.synchronize()
         got = sets[0]["c"].cpu().view(torch.int16).numpy().view(np.uint16).reshape(L, M)
         ref = oracle.gemv(inp0, layout, nthreads=min(os.cpu_count() or 1, 16))
         verified = bool(oracle.check(got, ref).all())
         log(f"parity vs oracle on set 0: {'ok' if verified else 'FAILED'}")
 
-    # ---- timed region: exactly K steps in one graph
+    # ---- warmup, then the timed region: exactly K steps in one graph replay
     K_steps = args.steps
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.graph(graph, stream=cap):
-        for i in range(K_steps):
-            step(i)
-    torch.cuda.synchronize()
-    graph.replay()                       # untimed replay: graph upload
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
-    graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
+    ms_per_step, warm = timed_graph(step, K_steps, args.warmup)
     wall_s = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / K_steps
-    log(f"timed: {K_steps} steps, {gpu_ms:.3f} ms GPU ({wall_s * 1e3:.3f} ms wall)")
+    log(f"timed: {K_steps} steps after {warm} warmup steps, {ms_per_step * K_steps:.3f} ms GPU "
+        f"({wall_s * 1e3:.1f} ms wall incl. capture and warmup)")
 
     # ---- per-kernel durations: eager launches bracketed by events
     st = torch.cuda.current_stream()
@@ -385,7 +369,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K_steps,
-        "warmup": args.warmup,
+        "warmup": warm,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",

@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # no packed-fp32 instructions: write plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # preload the leading kernel arguments into SGPRs (the GEMV kernel puts
+    # the scalars its first loads depend on there)
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
 ]
 
 

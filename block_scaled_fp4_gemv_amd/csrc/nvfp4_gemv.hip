@@ -176,10 +176,15 @@ __device__ __attribute__((always_inline)) inline void copy16_to_lds(const void *
 }
 #pragma clang diagnostic pop
 
+// The scalars that the first loads of A depend on lead the argument list as
+// plain scalars: the build preloads the leading kernel arguments into SGPRs
+// (kernarg preload), so the A stream does not wait for a kernarg read at wave
+// start. Params repeats them for the host side; the kernel uses these copies.
 template <int LAYOUT, int LPR, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
-    const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
+    const uint8_t *__restrict__ A, uint32_t n_wg, int32_t M, int32_t K, int32_t nL, int32_t spw,
+    int32_t ns, int32_t kc_split, int32_t a_row, int64_t a_extent, int32_t P, int32_t stage_bytes,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
     uint16_t *__restrict__ C, Params p)
 {
     constexpr int SEG = LPR * kCpl;              // chunks per K-segment
@@ -190,21 +195,20 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     constexpr int DR = kDeferRounds;             // first rounds that keep their block sums
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t lid = xcd_remap(blockIdx.x, n_wg);
     const int32_t s = SPLIT ? (int32_t)(lid % (uint32_t)p.S) : 0;
     const uint32_t t2 = SPLIT ? lid / (uint32_t)p.S : lid;
-    const int32_t tile = p.L == 1 ? (int32_t)t2 : (int32_t)(t2 % (uint32_t)p.P);
-    const int32_t l = p.L == 1 ? 0 : (int32_t)(t2 / (uint32_t)p.P);
+    const int32_t tile = nL == 1 ? (int32_t)t2 : (int32_t)(t2 % (uint32_t)P);
+    const int32_t l = nL == 1 ? 0 : (int32_t)(t2 / (uint32_t)P);
 
-    const int32_t M = p.M, K = p.K;
     const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
     // Slots of this workgroup: a contiguous range, so that its blocked scales
     // are few whole lines per 512-byte tile (neighbouring slots share a line).
-    const int32_t first = tile * p.spw;
-    const int32_t nslots = min(p.spw, p.ns - first);
+    const int32_t first = tile * spw;
+    const int32_t nslots = min(spw, ns - first);
     const int32_t nq = 4 * nslots;                        // local rows (some may be >= M)
-    const int32_t c_begin = s * p.kc_split;
-    const int32_t c_end = min(c_begin + p.kc_split, nchunks);
+    const int32_t c_begin = s * kc_split;
+    const int32_t c_end = min(c_begin + kc_split, nchunks);
 
     // One wave stages the scales, the others compute.
     // A wave's vector loads complete in order, so scale loads issued by a
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     constexpr int BSTB = kStageB ? (64 * LPR + kDmaBytes - 1) / kDmaBytes * kDmaBytes : 0;   // staged B bytes
     constexpr int SFBB = (32 * LPR + kDmaBytes - 1) / kDmaBytes * kDmaBytes;   // staged blocked SFB bytes
     uint8_t *stage = lds;                                  // staged SFA of the segment
-    uint8_t *b_stage = lds + p.stage_bytes;                // staged B of the segment: chunk c at c*16
+    uint8_t *b_stage = lds + stage_bytes;                  // staged B of the segment: chunk c at c*16
     uint8_t *sfb_stage = b_stage + BSTB;                   // staged blocked SFB: 4-block group g at g*16
     float *part = (float *)(sfb_stage + SFBB);             // [nq][WPG] per-wave row sums
 
@@ -243,9 +247,11 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     // first 128-row block: 32-bit lane offsets (the rows of one workgroup lie
     // within a few blocks).
     const int32_t row_base = (first >> 5) << 7;
-    const int64_t a_begin = (int64_t)l * p.a_batch + (int64_t)row_base * p.a_row;
+    int64_t a_begin = (int64_t)row_base * a_row;
+    if (nL != 1)                                           // one batch: no kernarg read here
+        a_begin += (int64_t)l * p.a_batch;
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A + a_begin), (short)0, (int)min(p.a_extent - a_begin, (int64_t)0x7FFFFFFF),
+        (void *)(A + a_begin), (short)0, (int)min(a_extent - a_begin, (int64_t)0x7FFFFFFF),
         kBufferFlags);
 
     const int32_t NR = (nq + G - 1) / G;                   // row rounds per group
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         auto row_off = [&](int32_t n) -> uint32_t {
             const int32_t q = min(grp + G * n, nq - 1);
             const int32_t r = min(slot_row(first, q), M - 1);
-            return (uint32_t)(r - row_base) * (uint32_t)p.a_row;
+            return (uint32_t)(r - row_base) * (uint32_t)a_row;
         };
         // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
         // the end read a clamped (valid) chunk so that every load is
@@ -538,7 +544,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);     // this wave's partial stores are done
     __syncthreads();
     if (tid == 0) {
-        uint32_t *ctr = &p.counters[(int64_t)l * p.P + tile];
+        uint32_t *ctr = &p.counters[(int64_t)l * P + tile];
         const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = prev == (uint32_t)(p.S - 1);
         if (last)
@@ -693,11 +699,13 @@ hipError_t launch_lpr(const Plan &pl, const void *a, const void *b, const void *
     const dim3 grid((uint32_t)pl.n_wg), block(kBlock);
     if (pl.S > 1)
         hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, true>), grid, block, pl.lds_bytes, st,
-                           (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
+                           (const uint8_t *)a, (uint32_t)pl.n_wg, p.M, p.K, p.L, p.spw, p.ns, p.kc_split,
+                           p.a_row, p.a_extent, p.P, p.stage_bytes, (const uint8_t *)b, (const uint8_t *)sfa,
                            (const uint8_t *)sfb, (uint16_t *)c, p);
     else
         hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, false>), grid, block, pl.lds_bytes, st,
-                           (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
+                           (const uint8_t *)a, (uint32_t)pl.n_wg, p.M, p.K, p.L, p.spw, p.ns, p.kc_split,
+                           p.a_row, p.a_extent, p.P, p.stage_bytes, (const uint8_t *)b, (const uint8_t *)sfa,
                            (const uint8_t *)sfb, (uint16_t *)c, p);
     return hipGetLastError();
 }

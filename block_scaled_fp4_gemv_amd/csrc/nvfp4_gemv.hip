@@ -105,12 +105,21 @@ struct Params {
     float *partials;      // [L*M][S] when S > 1
 };
 
-// Row of local row q of a workgroup whose first slot is first: slot
-// first + q/4, sub-row q%4 (the 32-row group inside the 128-row block).
-__device__ inline int32_t slot_row(int32_t first, int32_t q)
+// Local row q of a workgroup whose slots are first .. first+nslots-1: sub-row
+// i4 = q / nslots (the 32-row group inside the 128-row block) of slot
+// first + q % nslots. Consecutive q are consecutive rows of A, so the rows a
+// workgroup streams at one time are neighbours in memory.
+__device__ inline void split_local_row(int32_t q, int32_t nslots, int32_t &sl, int32_t &i4)
 {
-    const int32_t s = first + (q >> 2);
-    return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31);
+    i4 = (q >= nslots) + (q >= 2 * nslots) + (q >= 3 * nslots);   // q < 4 * nslots
+    sl = q - i4 * nslots;
+}
+__device__ inline int32_t slot_row(int32_t first, int32_t nslots, int32_t q)
+{
+    int32_t sl, i4;
+    split_local_row(q, nslots, sl, i4);
+    const int32_t s = first + sl;
+    return ((s >> 5) << 7) + (i4 << 5) + (s & 31);
 }
 
 // Byte offset of the two scales of chunk c (blocks 2c, 2c+1) of row r.
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                             const int32_t sg = first + mn;
                             src = sfa_l + ((int64_t)(sg >> 5) * ncb + cb0 + mjc) * 512 + (sg & 31) * 16;
                         } else {
-                            const int32_t r = min(slot_row(first, mjc), M - 1);
+                            const int32_t r = min(slot_row(first, nslots, mjc), M - 1);
                             src = sfa_l + (int64_t)r * p.sfa_row + 2 * c0 + 16 * mn;
                         }
                         copy16_to_lds(src, stage + i * kDmaBytes);
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 // plain scales whose rows are not 16-byte multiples: 2 bytes at a time
                 for (int32_t it = lane; it < nq * nck; it += 64) {
                     const int32_t q = it / nck, c = it % nck;
-                    const int32_t r = min(slot_row(first, q), M - 1);
+                    const int32_t r = min(slot_row(first, nslots, q), M - 1);
                     *(uint16_t *)(stage + 2 * it) = *(const uint16_t *)(sfa_l + (int64_t)r * p.sfa_row + 2 * (c0 + c));
                 }
             }
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
 
         auto row_off = [&](int32_t n) -> uint32_t {
             const int32_t q = min(grp + G * n, nq - 1);
-            const int32_t r = min(slot_row(first, q), M - 1);
+            const int32_t r = min(slot_row(first, nslots, q), M - 1);
             return (uint32_t)(r - row_base) * (uint32_t)a_row;
         };
         // Step t = chunk t % kCpl of the group's row round t / kCpl; steps past
@@ -381,7 +390,9 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         }
         auto sfa_of = [&](int32_t n) -> uint4_t {         // the lane's 4 scale pairs of round n
             const int32_t q = min(grp + G * n, nq - 1);
-            const uint32_t rowpart = LAYOUT == NVFP4_SF_BLOCKED ? (uint32_t)((q >> 2) * 16 + (q & 3) * 4)
+            int32_t sl, i4;
+            split_local_row(q, nslots, sl, i4);
+            const uint32_t rowpart = LAYOUT == NVFP4_SF_BLOCKED ? (uint32_t)(sl * 16 + i4 * 4)
                                                                 : (uint32_t)(q * nck * 2);
             uint4_t w;
             w.x = *(const uint16_t *)(stage + sfoff[0] + rowpart);
@@ -510,7 +521,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     // ---- per-row totals: add the per-wave sums in a fixed order, round once
     if (!SPLIT) {
         for (int32_t q = tid; q < nq; q += kThreads) {
-            const int32_t r = slot_row(first, q);
+            const int32_t r = slot_row(first, nslots, q);
             if (r < M) {
                 float v = part[q * WPG];
 #pragma unroll
@@ -530,7 +541,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     // ticket is taken. Agent-scope fences are avoided on purpose: on this chip
     // they write back and invalidate the whole L2 of the XCD, once per workgroup.
     for (int32_t q = tid; q < nq; q += kThreads) {
-        const int32_t r = slot_row(first, q);
+        const int32_t r = slot_row(first, nslots, q);
         if (r < M) {
             float v = part[q * WPG];
 #pragma unroll
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     if (!is_last)
         return;
     for (int32_t q = tid; q < nq; q += kThreads) {
-        const int32_t r = slot_row(first, q);
+        const int32_t r = slot_row(first, nslots, q);
         if (r < M) {
             const float *pp = p.partials + (abatch + r) * p.S;
             float v = 0.0f;

@@ -36,9 +36,17 @@ def xcd_remap(i, n):
     return x * q + np.minimum(x, r) + j
 
 
-def slot_row(first, q):
-    s = first + (q >> 2)
-    return ((s >> 5) << 7) + ((q & 3) << 5) + (s & 31)
+def split_local_row(q, nslots):
+    """Local row q of a workgroup -> (slot offset, 32-row group): run by run."""
+    q = np.asarray(q)
+    i4 = (q >= nslots).astype(np.int64) + (q >= 2 * nslots) + (q >= 3 * nslots)
+    return q - i4 * nslots, i4
+
+
+def slot_row(first, nslots, q):
+    sl, i4 = split_local_row(q, nslots)
+    s = first + sl
+    return ((s >> 5) << 7) + (i4 << 5) + (s & 31)
 
 
 def stage_bytes(lpr, spw):
@@ -118,14 +126,14 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
         a_begin = l * a_bat + row_base * a_row
         num_records = min(a_bytes - a_begin, 2 ** 31 - 1)
         nsteps = cdiv(nq, G) * CPL
-        rows_all = slot_row(first, np.arange(nq))
+        rows_all = slot_row(first, nslots, np.arange(nq))
         for c0 in range(c_begin, c_end, SEG):
             nck = min(SEG, c_end - c0)
             # ---- A: every step, including the prefetch issued past the end
             last = cdiv(nsteps, PREFETCH) * PREFETCH + PREFETCH
             for t in range(last):
                 q = np.minimum(grp + G * (t // CPL), nq - 1)
-                r = np.minimum(slot_row(first, q), M - 1)
+                r = np.minimum(slot_row(first, nslots, q), M - 1)
                 ci = c0 + np.minimum(j + (t % CPL) * lpr, nck - 1)
                 off = (r - row_base) * a_row + ci * 16
                 assert off.min() >= 0 and (off + 16).max() <= num_records, "A read outside the resource"
@@ -145,7 +153,7 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
                         src = l * sfa_bat + ((sg >> 5) * ncb + cb0 + cb) * 512 + (sg & 31) * 16
                     else:
                         q, u = np.minimum(it // units, nq - 1), it % units
-                        r = np.minimum(slot_row(first, q), M - 1)
+                        r = np.minimum(slot_row(first, nslots, q), M - 1)
                         assert (2 * c0 + 16 * u + 16).max() <= nkb
                         src = l * sfa_bat + r * sfa_row + 2 * c0 + 16 * u
                         assert (src % 16 == 0).all(), "16-byte staging copy from an unaligned address"
@@ -161,7 +169,7 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
             else:
                 it = np.arange(nq * nck)
                 q, c = it // nck, it % nck
-                r = np.minimum(slot_row(first, q), M - 1)
+                r = np.minimum(slot_row(first, nslots, q), M - 1)
                 src = l * sfa_bat + r * sfa_row + 2 * (c0 + c)
                 assert src.min() >= 0 and (src + 2).max() <= sfa_size
                 assert (src % 2 == 0).all()
@@ -211,7 +219,8 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
             # the 2 bytes at sfoff(c) + rowpart(q) (c, q clamped as in the kernel)
             def staged_at(q, c):
                 if layout == 1:
-                    return (c >> 1) * nslots * 16 + (c & 1) * 2 + (q >> 2) * 16 + (q & 3) * 4
+                    sl, i4 = split_local_row(q, nslots)
+                    return (c >> 1) * nslots * 16 + (c & 1) * 2 + sl * 16 + i4 * 4
                 return (q * nck + c) * 2
             for k in range(CPL):
                 cc = np.minimum(j + k * lpr, nck - 1)

@@ -421,8 +421,9 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         // One round: block sums of the lane's chunks against b', then (SCALED)
         // the scales, the row sum and its store; the ring slot is refilled with
         // the step PR rounds ahead.
-        auto round = [&](auto scaled, int32_t n, int rr, int dn) {
+        auto round = [&](auto scaled, auto refill, int32_t n, int rr, int dn) {
             constexpr bool SCALED = decltype(scaled)::value;
+            constexpr bool REFILL = decltype(refill)::value;      // the last rounds have nothing to load
             const uint32_t ro_refill = row_off(n + PR);
             float2_t sfk[kCpl];
             if (SCALED) {
@@ -450,7 +451,8 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 // refill the slot only after its last use: a load hoisted above
                 // the use would need a second register set and copies that wait
                 __builtin_amdgcn_sched_barrier(0);
-                abuf[u] = load_a(arsrc, ro_refill + choff[k]);
+                if (REFILL)
+                    abuf[u] = load_a(arsrc, ro_refill + choff[k]);
             }
             if (SCALED)
                 store_row(grp + G * n, acc);
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         // rounds 0 .. DR-1 keep their block sums (straight-line code)
 #pragma unroll
         for (int n = 0; n < DR; ++n)
-            round(std::false_type{}, n, n % PR, n);
+            round(std::false_type{}, std::true_type{}, n, n % PR, n);
 
         __syncthreads();                                   // the staged scales are published
 
@@ -510,10 +512,17 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         // at the loop entry the youngest loads are A loads, as on the loop's
         // back edge, so its waits stay exact
         sf_next = sfa_of(DR);
-        for (int32_t n0 = DR; n0 < NR; n0 += PR) {
+        int32_t n0 = DR;
+        for (; n0 + PR < NR; n0 += PR) {
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr)
-                round(std::true_type{}, n0 + rr, rr, 0);
+                round(std::true_type{}, std::true_type{}, n0 + rr, rr, 0);
+        }
+        // the last ring of rounds: every row is loaded, nothing to refill
+        if (n0 < NR) {
+#pragma unroll
+            for (int rr = 0; rr < PR; ++rr)
+                round(std::true_type{}, std::false_type{}, n0 + rr, rr, 0);
         }
     }
     __syncthreads();

@@ -343,6 +343,29 @@ def main():
     log(f"timed: {K_steps} steps after {warm} warmup steps, {ms_per_step * K_steps:.3f} ms GPU "
         f"({wall_s * 1e3:.1f} ms wall incl. capture and warmup)")
 
+    # ---- attainable: a plain streaming read of the same byte count (rounded
+    # down to 256 KiB), same pattern, same launch and timing method
+    rd_bytes = w.ideal_bytes // (256 * 1024) * (256 * 1024)
+    attainable = None
+    if rd_bytes > 0:
+        rd_sets = max(1, min(64, -(-ROTATE_BYTES // rd_bytes)))
+        # random bytes, like the GEMV's operands (HBM power, and so clocks, depend on the data)
+        rd_gen = torch.Generator(device=dev)
+        rd_gen.manual_seed(12345)
+        rd_bufs = [torch.randint(0, 256, (rd_bytes,), dtype=torch.uint8, device=dev, generator=rd_gen)
+                   for _ in range(rd_sets)]
+        sink = torch.zeros(256, dtype=torch.int32, device=dev)
+
+        def rd_step(i, stream=None):
+            g.nvfp4_stream_read(rd_bufs[i % rd_sets], rd_bytes, sink, stream)
+        rd_ms, _ = timed_graph(rd_step, K_steps, args.warmup)
+        rd_gbs = rd_bytes / (rd_ms * 1e-3) / 1e9
+        attainable = {"kind": "nvfp4_stream_read: one streaming read of the same byte count",
+                      "bytes": rd_bytes, "us_per_call": round(rd_ms * 1e3, 3), "GB/s": round(rd_gbs, 2),
+                      "pct_of_peak": round(100 * rd_gbs / PEAK_HBM_GBS, 2)}
+        log(f"attainable: streaming read of {rd_bytes} B: {rd_ms * 1e3:.3f} us per call, {rd_gbs:.0f} GB/s")
+        del rd_bufs
+
     # ---- per-kernel durations: eager launches bracketed by events
     st = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
@@ -384,6 +407,9 @@ def main():
                       "min": round(float(durs_us.min()), 3),
                       "p90": round(float(np.percentile(durs_us, 90)), 3)},
         "verified_vs_oracle": verified,
+        "attainable": attainable,
+        # GB/s of the GEMV over GB/s of the streaming read
+        "pct_of_attainable": round(100 * value_gbs / attainable["GB/s"], 2) if attainable else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},

@@ -11,7 +11,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("nvfp4_gemv.hip", "nvfp4_reblock.hip", "nvfp4_gemm_small_n.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("nvfp4_gemv.hip", "nvfp4_reblock.hip", "nvfp4_gemm_small_n.hip",
+                                                    "nvfp4_stream_read.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4gemv.so")
 

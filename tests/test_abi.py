@@ -270,3 +270,14 @@ def test_small_n_plan():
     assert p["lds_bytes"] <= 48 * 1024
     with pytest.raises(g.Nvfp4Error):
         g.nvfp4_gemm_small_n_plan(128, 9, 256, 1)
+
+
+def test_stream_read_validation():
+    L = g.lib()
+    unit = 256 * 1024
+    assert L.nvfp4_stream_read(None, unit, A16, None) == g.NVFP4_ERR_NULL_POINTER
+    assert L.nvfp4_stream_read(A16, unit, None, None) == g.NVFP4_ERR_NULL_POINTER
+    for bad in (0, unit - 16, unit + 1024):
+        assert L.nvfp4_stream_read(A16, bad, A16, None) == g.NVFP4_ERR_INVALID_SHAPE, bad
+    assert L.nvfp4_stream_read(A16 + 8, unit, A16, None) == g.NVFP4_ERR_MISALIGNED
+    assert L.nvfp4_stream_read(A16, unit, A16 + 2, None) == g.NVFP4_ERR_MISALIGNED

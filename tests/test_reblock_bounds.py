@@ -2,7 +2,9 @@
 run over its whole grid before it runs on a GPU: every plain read and every
 blocked write is inside its buffer, every blocked byte is written exactly once,
 and the bytes written are the view chain's (padding 0). Keep in step with the
-kernel: 256 threads, 16 tiles per workgroup, 16 words per row in LDS."""
+kernel: 256 threads, 16 tiles per workgroup, 16 words per row in LDS, rows
+read in 16-byte units when the row length is a multiple of 16 (and the input
+16-byte aligned), else in words or bytes."""
 import numpy as np
 import pytest
 
@@ -12,8 +14,10 @@ import synth
 THREADS, TILES = 256, 16
 
 
-def emulate(plain, rows, K, L):
+def emulate(plain, rows, K, L, aligned=True):
     cols = K // 16
+    uw = 4 if (aligned and cols % 16 == 0) else 1      # words per read unit
+    upr = TILES // uw
     nrb, ncb = -(-rows // 128), -(-cols // 4)
     wg_per_rb = -(-ncb // TILES)
     out_batch = nrb * ncb * 512
@@ -27,17 +31,20 @@ def emulate(plain, rows, K, L):
         assert l < L
         cb0 = wg * TILES
         words = np.zeros((128, TILES), np.uint32)
-        for i in range(128 * TILES // THREADS):
+        for i in range(128 * upr // THREADS):
             e = t + i * THREADS
-            row, wd = e // TILES, e % TILES
-            r, cb = rb * 128 + row, cb0 + wd
-            for rr, cc, rw, w in zip(r, cb, row, wd):
+            row, u = e // upr, e % upr
+            r, cb = rb * 128 + row, cb0 + u * uw
+            for rr, cc, rw, uu in zip(r, cb, row, u):
                 if rr >= rows or 4 * cc >= cols:
                     continue
-                n = min(4, cols - 4 * cc)
+                n = 16 if uw == 4 else min(4, cols - 4 * cc)
                 src = l * rows * cols + rr * cols + 4 * cc
                 assert 0 <= src and src + n <= flat.size, "plain read outside the buffer"
-                words[rw, w] = int.from_bytes(flat[src:src + n].tobytes(), "little")
+                assert uw == 1 or src % 16 == 0, "16-byte read from an unaligned offset"
+                got = np.zeros(4 * uw, np.uint8)
+                got[:n] = flat[src:src + n]
+                words[rw, uu * uw:uu * uw + uw] = got.view(np.uint32)
         for i in range(TILES * 32 // THREADS):
             e = t + i * THREADS
             tl, r32 = e // 32, e % 32
@@ -53,10 +60,12 @@ def emulate(plain, rows, K, L):
 
 
 @pytest.mark.parametrize("rows,K,L", [(1, 32, 1), (1, 96, 2), (127, 4096, 1), (128, 2048, 2),
-                                      (300, 4128, 1), (129, 32, 3), (7, 1056, 2)])
-def test_reblock_kernel_indexing(rows, K, L):
+                                      (300, 4128, 1), (129, 32, 3), (7, 1056, 2), (130, 8192, 1),
+                                      (5, 16640, 2)])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_reblock_kernel_indexing(rows, K, L, aligned):
     plain = np.random.default_rng(rows * K + L).integers(0, 256, (L, rows, K // 16), dtype=np.uint8)
-    out, writes = emulate(plain, rows, K, L)
+    out, writes = emulate(plain, rows, K, L, aligned)
     assert np.all(writes == 1), "each blocked byte is written exactly once"
     np.testing.assert_array_equal(out, synth.to_blocked(plain, pad=0))
     assert out.size == g.nvfp4_blocked_scales_bytes(rows, K, L)

@@ -233,6 +233,12 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
         return NVFP4_ERR_MISALIGNED;
     if (!std::isfinite(alpha))
         return NVFP4_ERR_INVALID_SCALE;
+    // One vector is the GEMV, whose kernel streams A faster (several chunks
+    // per lane and row, one reduction per row): use it whenever its plan needs
+    // no split-K workspace, so that this entry point still allocates nothing.
+    // The operand layouts for N = 1 are the GEMV's.
+    if (N == 1 && nvfp4_gemv_workspace_bytes(M, K, L) == 0)
+        return nvfp4_gemv_scaled(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, nullptr, 0, stream);
     SnParams p{};
     p.M = (int32_t)M;
     p.K = (int32_t)K;

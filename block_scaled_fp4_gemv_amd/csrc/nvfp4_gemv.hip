@@ -75,6 +75,7 @@ constexpr int kDmaBytes = 64 * 16;        // LDS bytes one wave-wide 16-byte dir
 constexpr bool kStageB = true;            // blocked layout: B is staged with SFB (else the computing waves load it)
 constexpr int kSfaAhead = 20;             // blocked: A-scale copies issued before the wait for b's inputs
 constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
+constexpr int kBFirstMaxRounds = 8;       // b's inputs go first for workgroups of at most this many row rounds
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
 constexpr int kCachePolicyNT = 2;         // buffer load cache policy: non-temporal
@@ -189,7 +190,11 @@ __device__ __attribute__((always_inline)) inline void copy16_to_lds(const void *
 // plain scalars: the build preloads the leading kernel arguments into SGPRs
 // (kernarg preload), so the A stream does not wait for a kernarg read at wave
 // start. Params repeats them for the host side; the kernel uses these copies.
-template <int LAYOUT, int LPR, bool SPLIT>
+// BFIRST: b's inputs are requested before the first ring of A (the staging
+// wave's copies behind a barrier, or the computing waves' own loads). That
+// pays when a workgroup has few row rounds, so the b' start-up is most of its
+// time; with many rounds, A first streams better.
+template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST>
 __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const uint8_t *__restrict__ A, uint32_t n_wg, int32_t M, int32_t K, int32_t nL, int32_t spw,
     int32_t ns, int32_t kc_split, int32_t a_row, int64_t a_extent, int32_t P, int32_t stage_bytes,
@@ -294,6 +299,8 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
             for (int32_t i = 0; i < nsfb; ++i)
                 copy16_to_lds(sfb_l + (int64_t)(cb0 + min(i * 64 + lane, ncb_seg - 1)) * 512,
                               sfb_stage + i * kDmaBytes);
+            if (BFIRST && STAGE_SFB)
+                __syncthreads();                           // b's input copies are issued
             if (!direct) {
                 // Wave-wide direct-to-LDS load i puts item i*64 + lane at
                 // (i*64 + lane) * 16; all loads are in flight at once. Item it
@@ -458,12 +465,16 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 store_row(grp + G * n, acc);
         };
 
-        // ---- the first kPrefetch steps of A, then b' (A first: the stream
-        // starts sooner, and b' waits for its inputs anyway)
+        // ---- the first kPrefetch steps of A and b's inputs, in the order
+        // BFIRST picks (b' waits for its inputs either way)
+        auto issue_ring = [&]() {
 #pragma unroll
-        for (int u = 0; u < kPrefetch; ++u)
-            abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int u = 0; u < kPrefetch; ++u)
+                abuf[u] = load_a(arsrc, row_off(u / kCpl) + choff[u % kCpl]);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if (!BFIRST)
+            issue_ring();
         uint4_t bload[kCpl];
         uint32_t sload[kCpl];
 #pragma unroll
@@ -475,6 +486,11 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (BFIRST) {
+            if (STAGE_SFB)
+                __syncthreads();                           // b's input copies are issued
+            issue_ring();
+        }
         if (STAGE_SFB) {
             __syncthreads();                               // b' inputs are staged
 #pragma unroll
@@ -597,6 +613,7 @@ struct Plan {
     int ns;               // slots per batch
     int stage_bytes;      // LDS bytes of staged scales
     int wide_plain;
+    int bfirst;           // b's inputs before the first ring of A (few row rounds per workgroup)
     int64_t n_wg;
     int lds_bytes;
     size_t ws_partials;   // bytes of float32 partials (after the ticket region)
@@ -703,6 +720,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
     pl.lds_bytes = (int)(pl.stage_bytes + (kStageB ? align_up((size_t)(64 * pl.lpr), kDmaBytes) : 0) +
                          align_up((size_t)(32 * pl.lpr), kDmaBytes) + 4 * spw * wpg * (int)sizeof(float));
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
+    // row rounds of a full workgroup: 4*spw rows, kThreads/lpr rows per round
+    pl.bfirst = cdiv(4 * spw * pl.lpr, kThreads) <= kBFirstMaxRounds ? 1 : 0;
     if (S > 1) {
         pl.ws_partials = align_up((size_t)(L * M * S) * sizeof(float), kWsAlign);
         pl.ws_total = kCounterBytes + pl.ws_partials;
@@ -712,22 +731,27 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
 
 thread_local int g_last_hip_error = 0;
 
+template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST>
+hipError_t launch_kernel(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
+                         void *c, const Params &p, hipStream_t st)
+{
+    const dim3 grid((uint32_t)pl.n_wg), block(kBlock);
+    hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, SPLIT, BFIRST>), grid, block, pl.lds_bytes, st,
+                       (const uint8_t *)a, (uint32_t)pl.n_wg, p.M, p.K, p.L, p.spw, p.ns, p.kc_split,
+                       p.a_row, p.a_extent, p.P, p.stage_bytes, (const uint8_t *)b, (const uint8_t *)sfa,
+                       (const uint8_t *)sfb, (uint16_t *)c, p);
+    return hipGetLastError();
+}
+
 template <int LAYOUT, int LPR>
 hipError_t launch_lpr(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                       void *c, const Params &p, hipStream_t st)
 {
-    const dim3 grid((uint32_t)pl.n_wg), block(kBlock);
     if (pl.S > 1)
-        hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, true>), grid, block, pl.lds_bytes, st,
-                           (const uint8_t *)a, (uint32_t)pl.n_wg, p.M, p.K, p.L, p.spw, p.ns, p.kc_split,
-                           p.a_row, p.a_extent, p.P, p.stage_bytes, (const uint8_t *)b, (const uint8_t *)sfa,
-                           (const uint8_t *)sfb, (uint16_t *)c, p);
-    else
-        hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, false>), grid, block, pl.lds_bytes, st,
-                           (const uint8_t *)a, (uint32_t)pl.n_wg, p.M, p.K, p.L, p.spw, p.ns, p.kc_split,
-                           p.a_row, p.a_extent, p.P, p.stage_bytes, (const uint8_t *)b, (const uint8_t *)sfa,
-                           (const uint8_t *)sfb, (uint16_t *)c, p);
-    return hipGetLastError();
+        return pl.bfirst ? launch_kernel<LAYOUT, LPR, true, true>(pl, a, b, sfa, sfb, c, p, st)
+                         : launch_kernel<LAYOUT, LPR, true, false>(pl, a, b, sfa, sfb, c, p, st);
+    return pl.bfirst ? launch_kernel<LAYOUT, LPR, false, true>(pl, a, b, sfa, sfb, c, p, st)
+                     : launch_kernel<LAYOUT, LPR, false, false>(pl, a, b, sfa, sfb, c, p, st);
 }
 
 template <int LAYOUT>

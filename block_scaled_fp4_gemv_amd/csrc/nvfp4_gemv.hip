@@ -194,7 +194,10 @@ __device__ __attribute__((always_inline)) inline void copy16_to_lds(const void *
 // wave's copies behind a barrier, or the computing waves' own loads). That
 // pays when a workgroup has few row rounds, so the b' start-up is most of its
 // time; with many rounds, A first streams better.
-template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST>
+// ILV: the deferred rounds are finished one per following round instead of
+// all at once after the publish barrier (measured faster for workgroups with
+// many row rounds and LPR <= 64, slower with LPR = 128 or few rounds).
+template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST, bool ILV>
 __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const uint8_t *__restrict__ A, uint32_t n_wg, int32_t M, int32_t K, int32_t nL, int32_t spw,
     int32_t ns, int32_t kc_split, int32_t a_row, int64_t a_extent, int32_t P, int32_t stage_bytes,
@@ -512,23 +515,52 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
 
         __syncthreads();                                   // the staged scales are published
 
-        // finish the first rounds, then the rest with the scales read one round ahead
-#pragma unroll
-        for (int n = 0; n < DR; ++n) {
+        // finish the deferred rounds: all at once, or (ILV) one per round of
+        // the next DR rounds, so no burst of finishing work holds back refills
+        auto finish = [&](int d) {
             float2_t sfk[kCpl];
-            decode_sfa(sfa_of(n), sfk);
+            decode_sfa(sfa_of(d), sfk);
             float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < kCpl; ++k) {
-                const float nacc = __builtin_fmaf(bsum[n][k].y, sfk[k].y, __builtin_fmaf(bsum[n][k].x, sfk[k].x, acc));
+                const float nacc = __builtin_fmaf(bsum[d][k].y, sfk[k].y, __builtin_fmaf(bsum[d][k].x, sfk[k].x, acc));
                 acc = live[k] ? nacc : acc;
             }
-            store_row(grp + G * n, acc);
+            store_row(grp + G * d, acc);
+        };
+        if (!ILV) {
+#pragma unroll
+            for (int d = 0; d < DR; ++d)
+                finish(d);
         }
-        // at the loop entry the youngest loads are A loads, as on the loop's
-        // back edge, so its waits stay exact
+        // then the rest with the scales read one round ahead; at the loop
+        // entry the youngest loads are A loads, as on the loop's back edge, so
+        // its waits stay exact
         sf_next = sfa_of(DR);
         int32_t n0 = DR;
+        if (ILV) {
+#pragma unroll
+            for (int it = 0; it < DR / PR; ++it) {
+                if (n0 + PR < NR) {
+#pragma unroll
+                    for (int rr = 0; rr < PR; ++rr) {
+                        round(std::true_type{}, std::true_type{}, n0 + rr, rr, 0);
+                        finish(it * PR + rr);
+                    }
+                } else if (n0 < NR) {
+#pragma unroll
+                    for (int rr = 0; rr < PR; ++rr) {
+                        round(std::true_type{}, std::false_type{}, n0 + rr, rr, 0);
+                        finish(it * PR + rr);
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < PR; ++rr)
+                        finish(it * PR + rr);
+                }
+                n0 += PR;
+            }
+        }
         for (; n0 + PR < NR; n0 += PR) {
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr)
@@ -614,6 +646,7 @@ struct Plan {
     int stage_bytes;      // LDS bytes of staged scales
     int wide_plain;
     int bfirst;           // b's inputs before the first ring of A (few row rounds per workgroup)
+    int ilv;              // deferred rounds finished one per following round
     int64_t n_wg;
     int lds_bytes;
     size_t ws_partials;   // bytes of float32 partials (after the ticket region)
@@ -722,6 +755,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
     // row rounds of a full workgroup: 4*spw rows, kThreads/lpr rows per round
     pl.bfirst = cdiv(4 * spw * pl.lpr, kThreads) <= kBFirstMaxRounds ? 1 : 0;
+    pl.ilv = pl.lpr <= 64 && !pl.bfirst ? 1 : 0;
     if (S > 1) {
         pl.ws_partials = align_up((size_t)(L * M * S) * sizeof(float), kWsAlign);
         pl.ws_total = kCounterBytes + pl.ws_partials;
@@ -731,27 +765,36 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
 
 thread_local int g_last_hip_error = 0;
 
-template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST>
+template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST, bool ILV>
 hipError_t launch_kernel(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                          void *c, const Params &p, hipStream_t st)
 {
     const dim3 grid((uint32_t)pl.n_wg), block(kBlock);
-    hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, SPLIT, BFIRST>), grid, block, pl.lds_bytes, st,
+    hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, SPLIT, BFIRST, ILV>), grid, block, pl.lds_bytes, st,
                        (const uint8_t *)a, (uint32_t)pl.n_wg, p.M, p.K, p.L, p.spw, p.ns, p.kc_split,
                        p.a_row, p.a_extent, p.P, p.stage_bytes, (const uint8_t *)b, (const uint8_t *)sfa,
                        (const uint8_t *)sfb, (uint16_t *)c, p);
     return hipGetLastError();
 }
 
+template <int LAYOUT, int LPR, bool SPLIT>
+hipError_t launch_split(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
+                        void *c, const Params &p, hipStream_t st)
+{
+    if constexpr (LPR <= 64) {                             // the plan sets ilv only there, never with bfirst
+        if (pl.ilv)
+            return launch_kernel<LAYOUT, LPR, SPLIT, false, true>(pl, a, b, sfa, sfb, c, p, st);
+    }
+    return pl.bfirst ? launch_kernel<LAYOUT, LPR, SPLIT, true, false>(pl, a, b, sfa, sfb, c, p, st)
+                     : launch_kernel<LAYOUT, LPR, SPLIT, false, false>(pl, a, b, sfa, sfb, c, p, st);
+}
+
 template <int LAYOUT, int LPR>
 hipError_t launch_lpr(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                       void *c, const Params &p, hipStream_t st)
 {
-    if (pl.S > 1)
-        return pl.bfirst ? launch_kernel<LAYOUT, LPR, true, true>(pl, a, b, sfa, sfb, c, p, st)
-                         : launch_kernel<LAYOUT, LPR, true, false>(pl, a, b, sfa, sfb, c, p, st);
-    return pl.bfirst ? launch_kernel<LAYOUT, LPR, false, true>(pl, a, b, sfa, sfb, c, p, st)
-                     : launch_kernel<LAYOUT, LPR, false, false>(pl, a, b, sfa, sfb, c, p, st);
+    return pl.S > 1 ? launch_split<LAYOUT, LPR, true>(pl, a, b, sfa, sfb, c, p, st)
+                    : launch_split<LAYOUT, LPR, false>(pl, a, b, sfa, sfb, c, p, st);
 }
 
 template <int LAYOUT>

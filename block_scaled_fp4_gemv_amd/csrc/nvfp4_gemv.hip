@@ -21,11 +21,13 @@
 // the scales of the workgroup's rows into LDS with direct-to-LDS loads
 // (global_load_lds), all in flight at once. A wave's vector loads complete in order, so scale loads issued by a
 // computing wave would hold back every later A load of that wave; from a wave
-// of their own they stream beside A. The computing waves start on A at once:
-// the first rounds keep their exact block sums and take the scales after the
-// barrier that publishes them.
+// of their own they stream beside A. The computing waves start on A at once
+// (or, in the BFIRST variant for workgroups with few row rounds, right after
+// the copies of b's inputs are issued): the first rounds keep their exact
+// block sums and take the scales after the barrier that publishes them.
 //
-// Inside a workgroup, LPR lanes share a row; lane j of a row group owns the
+// Inside a workgroup, LPR lanes share a row and the rows are taken run by
+// run (consecutive rows of A at one time); lane j of a row group owns the
 // chunks j, j+LPR, j+2*LPR, j+3*LPR of every K-segment (4*LPR chunks), so each
 // wave-wide load is a contiguous run of 16-byte vectors. The lane converts its
 // four chunks of B into b'[k] = e2m1(B[k]) * e4m3(SFB[k/16]) once (float16 in
@@ -37,7 +39,7 @@
 //     float32 (multiples of sfb/4 below 2^12 * sfb);
 //   * one FMA per block applies the SFA scale (v_cvt_pk_f32_fp8 decode).
 // Rows follow each other without a break: the loads of the next kPrefetch
-// chunk-steps are always in flight. A row's lanes are summed with DPP and the
+// chunk-steps are in flight until the last ring, which refills nothing. A row's lanes are summed with DPP and the
 // per-wave sums are added in LDS in a fixed order; the result is rounded to
 // float16 once, after one float32 multiply by the global scale alpha (1 for
 // the unscaled entry points, where it changes nothing). K-split shapes (small

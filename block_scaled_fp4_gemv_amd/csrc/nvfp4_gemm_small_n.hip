@@ -34,7 +34,12 @@ constexpr int kSnWaves = kSnThreads / 64;
 constexpr int kSnRing = 8;                    // rows of A in flight per lane
 constexpr int kSnMaxN = 8;
 constexpr int kSnPartBudget = 48 * 1024;      // LDS bytes of per-wave row sums
-constexpr int64_t kSnTargetWGs = 256;
+// Workgroups to aim for: one per CU for N <= 2; two per CU from N = 3, where
+// the per-row lane reductions (dependent DPP chains) need a second wave per
+// SIMD to hide their latency (headline A, N = 4 / 8: 40.9 -> 35.7 / 68.8 ->
+// 54.0 us; N = 2: 27.8 -> 30.9, so it keeps one).
+constexpr int64_t kSnTargetWGsFew = 256;
+constexpr int64_t kSnTargetWGsMany = 512;
 
 struct SnParams {
     int32_t M, K, L;
@@ -197,10 +202,11 @@ nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t 
     if (M < 1 || N < 1 || N > kSnMaxN || L < 1 || K < 32 || K % 32 != 0 || K > (INT64_C(1) << 22) ||
         M > INT32_MAX / 2 || L > INT32_MAX / 2 || L * M > (INT64_C(1) << 62) / K)
         return NVFP4_ERR_INVALID_SHAPE;
-    // about kSnTargetWGs workgroups, each a contiguous row range of one batch,
+    // about the target number of workgroups, each a contiguous row range of one batch,
     // with the per-wave row sums inside the LDS budget
     const int64_t rmax = kSnPartBudget / (N * kSnWaves * (int64_t)sizeof(float));
-    int64_t P = std::min<int64_t>(M, std::max<int64_t>(1, kSnTargetWGs / L));
+    const int64_t target = N <= 2 ? kSnTargetWGsFew : kSnTargetWGsMany;
+    int64_t P = std::min<int64_t>(M, std::max<int64_t>(1, target / L));
     P = std::max<int64_t>(P, (M + rmax - 1) / rmax);
     const int64_t R = (M + P - 1) / P;
     P = (M + R - 1) / R;                                              // every workgroup has a row

@@ -264,8 +264,11 @@ def test_small_n_validation():
 
 
 def test_small_n_plan():
-    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1)
+    # one workgroup per CU for N <= 2, two from N = 3 (latency of the lane reductions)
+    p = g.nvfp4_gemm_small_n_plan(7168, 2, 16384, 1)
     assert p["workgroups"] == 256 and p["rows_per_wg"] == 28
+    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1)
+    assert p["workgroups"] == 512 and p["rows_per_wg"] == 14
     p = g.nvfp4_gemm_small_n_plan(100000, 8, 64, 1)
     assert p["lds_bytes"] <= 48 * 1024
     with pytest.raises(g.Nvfp4Error):

@@ -313,6 +313,12 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
     // The operand layouts for N = 1 are the GEMV's.
     if (N == 1 && nvfp4_gemv_workspace_bytes(M, K, L) == 0)
         return nvfp4_gemv_scaled(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, nullptr, 0, stream);
+    // Two vectors: the GEMV kernel with b' of both in registers, where it needs no K-split.
+    if (N == 2 && nvfp4_gemv_workspace_bytes(M, K, L) == 0) {
+        const nvfp4_status_t st2 = nvfp4_gemv_two_vectors(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, stream);
+        if (st2 != NVFP4_ERR_INVALID_SHAPE)
+            return st2;
+    }
     SnParams p{};
     p.M = (int32_t)M;
     p.K = (int32_t)K;

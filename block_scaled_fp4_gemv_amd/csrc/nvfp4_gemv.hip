@@ -103,6 +103,9 @@ struct Params {
     int64_t sfa_batch;    // bytes between batches of SFA
     int64_t sfb_batch;    // bytes between batches of SFB
     int64_t c_batch;      // float16 elements between batches of C
+    int64_t b_vec;        // bytes between the vectors of B (NV > 1)
+    int64_t sfb_vec;      // bytes between the vectors' scales in SFB (plain: a row; blocked: a 16-byte line)
+    int64_t c_vec;        // float16 elements between the vectors' columns of C
     float alpha;          // global scale, applied to the float32 row sum before rounding
     uint32_t *counters;   // tickets [L][P] when S > 1
     float *partials;      // [L*M][S] when S > 1
@@ -199,7 +202,9 @@ __device__ __attribute__((always_inline)) inline void copy16_to_lds(const void *
 // ILV: the deferred rounds are finished one per following round instead of
 // all at once after the publish barrier (measured faster for workgroups with
 // many row rounds and LPR <= 64, slower with LPR = 128 or few rounds).
-template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST, bool ILV>
+// NV: right-hand vectors (1, or 2 for the skinny GEMM): A is streamed and
+// decoded once and dotted with each vector's b'.
+template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST, bool ILV, int NV>
 __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     const uint8_t *__restrict__ A, uint32_t n_wg, int32_t M, int32_t K, int32_t nL, int32_t spw,
     int32_t ns, int32_t kc_split, int32_t a_row, int64_t a_extent, int32_t P, int32_t stage_bytes,
@@ -212,6 +217,7 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     constexpr int RED = LPR < 64 ? LPR : 64;     // lanes summed inside one wave
     constexpr int PR = kPrefetch / kCpl;         // row rounds in the load ring
     constexpr int DR = kDeferRounds;             // first rounds that keep their block sums
+    static_assert(NV == 1 || !SPLIT, "several vectors only without a K-split");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const uint32_t lid = xcd_remap(blockIdx.x, n_wg);
@@ -259,8 +265,8 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     constexpr int SFBB = (32 * LPR + kDmaBytes - 1) / kDmaBytes * kDmaBytes;   // staged blocked SFB bytes
     uint8_t *stage = lds;                                  // staged SFA of the segment
     uint8_t *b_stage = lds + stage_bytes;                  // staged B of the segment: chunk c at c*16
-    uint8_t *sfb_stage = b_stage + BSTB;                   // staged blocked SFB: 4-block group g at g*16
-    float *part = (float *)(sfb_stage + SFBB);             // [nq][WPG] per-wave row sums
+    uint8_t *sfb_stage = b_stage + NV * BSTB;              // staged blocked SFB: 4-block group g at g*16 (per vector)
+    float *part = (float *)(sfb_stage + NV * SFBB);        // [nq][NV][WPG] per-wave row sums
 
     // A through a buffer resource based at the first row of this workgroup's
     // first 128-row block: 32-bit lane offsets (the rows of one workgroup lie
@@ -299,11 +305,16 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
             // for the deferred rounds' end. Past the end the index clamps.
             const int32_t nbc = STAGE_B ? (nck + 63) >> 6 : 0;
             const int32_t nsfb = STAGE_SFB ? (ncb_seg + 63) >> 6 : 0;
-            for (int32_t i = 0; i < nbc; ++i)
-                copy16_to_lds(b_l + (int64_t)(c0 + min(i * 64 + lane, nck - 1)) * 16, b_stage + i * kDmaBytes);
-            for (int32_t i = 0; i < nsfb; ++i)
-                copy16_to_lds(sfb_l + (int64_t)(cb0 + min(i * 64 + lane, ncb_seg - 1)) * 512,
-                              sfb_stage + i * kDmaBytes);
+#pragma unroll
+            for (int nv = 0; nv < NV; ++nv)
+                for (int32_t i = 0; i < nbc; ++i)
+                    copy16_to_lds(b_l + nv * p.b_vec + (int64_t)(c0 + min(i * 64 + lane, nck - 1)) * 16,
+                                  b_stage + nv * BSTB + i * kDmaBytes);
+#pragma unroll
+            for (int nv = 0; nv < NV; ++nv)
+                for (int32_t i = 0; i < nsfb; ++i)
+                    copy16_to_lds(sfb_l + nv * p.sfb_vec + (int64_t)(cb0 + min(i * 64 + lane, ncb_seg - 1)) * 512,
+                                  sfb_stage + nv * SFBB + i * kDmaBytes);
             if (BFIRST && STAGE_SFB)
                 __syncthreads();                           // b's input copies are issued
             if (!direct) {
@@ -419,16 +430,16 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
             sfk[2] = __builtin_amdgcn_cvt_pk_f32_fp8(w.z, false);
             sfk[3] = __builtin_amdgcn_cvt_pk_f32_fp8(w.w, false);
         };
-        auto store_row = [&](int32_t q, float acc) {
+        auto store_row = [&](int32_t q, float acc, int nv) {
             const float v = group_sum<RED>(acc);
             if (leader && q < nq) {
-                float *dst = part + q * WPG + wig;
+                float *dst = part + (q * NV + nv) * WPG + wig;
                 *dst = first_seg ? v : *dst + v;
             }
         };
         uint4_t abuf[kPrefetch];
-        uint4_t bp[kCpl][4];
-        float2_t bsum[DR][kCpl];                           // block sums of the first rounds
+        uint4_t bp[NV][kCpl][4];
+        float2_t bsum[DR][kCpl][NV];                       // block sums of the first rounds
         uint4_t sf_next = {0u, 0u, 0u, 0u};
         // One round: block sums of the lane's chunks against b', then (SCALED)
         // the scales, the row sum and its store; the ring slot is refilled with
@@ -443,22 +454,43 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 sf_next = sfa_of(n + 1);
                 decode_sfa(sfc, sfk);
             }
-            float acc = 0.0f;
+            float acc[NV];
+#pragma unroll
+            for (int nv = 0; nv < NV; ++nv)
+                acc[nv] = 0.0f;
 #pragma unroll
             for (int k = 0; k < kCpl; ++k) {
                 const int u = rr * kCpl + k;
                 const uint4_t a = abuf[u];
-                const float lo = dot_block(a.x, a.y, bp[k][0], bp[k][1]);
-                const float hi = dot_block(a.z, a.w, bp[k][2], bp[k][3]);
-                if (SCALED) {
-                    const float nacc = __builtin_fmaf(hi, sfk[k].y, __builtin_fmaf(lo, sfk[k].x, acc));
-                    acc = live[k] ? nacc : acc;
+                if constexpr (NV == 1) {
+                    // (one vector: the same code as a plain loop body, so the
+                    // scheduler sees exactly the single-vector GEMV)
+                    const float lo = dot_block(a.x, a.y, bp[0][k][0], bp[0][k][1]);
+                    const float hi = dot_block(a.z, a.w, bp[0][k][2], bp[0][k][3]);
+                    if (SCALED) {
+                        const float nacc = __builtin_fmaf(hi, sfk[k].y, __builtin_fmaf(lo, sfk[k].x, acc[0]));
+                        acc[0] = live[k] ? nacc : acc[0];
+                    } else {
+                        // computed here, as the data arrives, not sunk to their use
+                        // after the staged scales
+                        float l2 = lo, h2 = hi;
+                        asm volatile("" : "+v"(l2), "+v"(h2));
+                        bsum[dn][k][0] = (float2_t){l2, h2};
+                    }
                 } else {
-                    // computed here, as the data arrives, not sunk to their use
-                    // after the staged scales
-                    float l2 = lo, h2 = hi;
-                    asm volatile("" : "+v"(l2), "+v"(h2));
-                    bsum[dn][k] = (float2_t){l2, h2};
+#pragma unroll
+                    for (int nv = 0; nv < NV; ++nv) {
+                        const float lo = dot_block(a.x, a.y, bp[nv][k][0], bp[nv][k][1]);
+                        const float hi = dot_block(a.z, a.w, bp[nv][k][2], bp[nv][k][3]);
+                        if (SCALED) {
+                            const float nacc = __builtin_fmaf(hi, sfk[k].y, __builtin_fmaf(lo, sfk[k].x, acc[nv]));
+                            acc[nv] = live[k] ? nacc : acc[nv];
+                        } else {
+                            float l2 = lo, h2 = hi;
+                            asm volatile("" : "+v"(l2), "+v"(h2));
+                            bsum[dn][k][nv] = (float2_t){l2, h2};
+                        }
+                    }
                 }
                 // refill the slot only after its last use: a load hoisted above
                 // the use would need a second register set and copies that wait
@@ -466,8 +498,11 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 if (REFILL)
                     abuf[u] = load_a(arsrc, ro_refill + choff[k]);
             }
-            if (SCALED)
-                store_row(grp + G * n, acc);
+            if (SCALED) {
+#pragma unroll
+                for (int nv = 0; nv < NV; ++nv)
+                    store_row(grp + G * n, acc[nv], nv);
+            }
         };
 
         // ---- the first kPrefetch steps of A and b's inputs, in the order
@@ -480,15 +515,18 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         };
         if (!BFIRST)
             issue_ring();
-        uint4_t bload[kCpl];
-        uint32_t sload[kCpl];
+        uint4_t bload[NV][kCpl];
+        uint32_t sload[NV][kCpl];
 #pragma unroll
-        for (int k = 0; k < kCpl; ++k) {
-            const int32_t ci = c0 + min(j + k * LPR, nck - 1);
-            if (!STAGE_B)
-                bload[k] = *(const uint4_t *)(b_l + (int64_t)ci * 16);
-            if (!STAGE_SFB)
-                sload[k] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
+        for (int nv = 0; nv < NV; ++nv) {
+#pragma unroll
+            for (int k = 0; k < kCpl; ++k) {
+                const int32_t ci = c0 + min(j + k * LPR, nck - 1);
+                if (!STAGE_B)
+                    bload[nv][k] = *(const uint4_t *)(b_l + nv * p.b_vec + (int64_t)ci * 16);
+                if (!STAGE_SFB)
+                    sload[nv][k] = *(const uint16_t *)(sfb_l + nv * p.sfb_vec + sf_pair_offset<LAYOUT>(0, ci, nkb, ncb));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         if (BFIRST) {
@@ -499,17 +537,23 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         if (STAGE_SFB) {
             __syncthreads();                               // b' inputs are staged
 #pragma unroll
-            for (int k = 0; k < kCpl; ++k) {
-                const int32_t cc = min(j + k * LPR, nck - 1);
-                if (STAGE_B)
-                    bload[k] = *(const uint4_t *)(b_stage + cc * 16);
-                sload[k] = *(const uint16_t *)(sfb_stage + (cc >> 1) * 16 + (cc & 1) * 2);
+            for (int nv = 0; nv < NV; ++nv) {
+#pragma unroll
+                for (int k = 0; k < kCpl; ++k) {
+                    const int32_t cc = min(j + k * LPR, nck - 1);
+                    if (STAGE_B)
+                        bload[nv][k] = *(const uint4_t *)(b_stage + nv * BSTB + cc * 16);
+                    sload[nv][k] = *(const uint16_t *)(sfb_stage + nv * SFBB + (cc >> 1) * 16 + (cc & 1) * 2);
+                }
             }
         }
         // b' for this lane's chunks of the segment (registers, reused for every row)
 #pragma unroll
-        for (int k = 0; k < kCpl; ++k)
-            make_bprime(bload[k], sload[k], bp[k]);
+        for (int nv = 0; nv < NV; ++nv) {
+#pragma unroll
+            for (int k = 0; k < kCpl; ++k)
+                make_bprime(bload[nv][k], sload[nv][k], bp[nv][k]);
+        }
         // rounds 0 .. DR-1 keep their block sums (straight-line code)
 #pragma unroll
         for (int n = 0; n < DR; ++n)
@@ -522,13 +566,17 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         auto finish = [&](int d) {
             float2_t sfk[kCpl];
             decode_sfa(sfa_of(d), sfk);
-            float acc = 0.0f;
 #pragma unroll
-            for (int k = 0; k < kCpl; ++k) {
-                const float nacc = __builtin_fmaf(bsum[d][k].y, sfk[k].y, __builtin_fmaf(bsum[d][k].x, sfk[k].x, acc));
-                acc = live[k] ? nacc : acc;
+            for (int nv = 0; nv < NV; ++nv) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kCpl; ++k) {
+                    const float nacc = __builtin_fmaf(bsum[d][k][nv].y, sfk[k].y,
+                                                      __builtin_fmaf(bsum[d][k][nv].x, sfk[k].x, acc));
+                    acc = live[k] ? nacc : acc;
+                }
+                store_row(grp + G * d, acc, nv);
             }
-            store_row(grp + G * d, acc);
         };
         if (!ILV) {
 #pragma unroll
@@ -582,11 +630,14 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
         for (int32_t q = tid; q < nq; q += kThreads) {
             const int32_t r = slot_row(first, nslots, q);
             if (r < M) {
-                float v = part[q * WPG];
 #pragma unroll
-                for (int w = 1; w < WPG; ++w)
-                    v += part[q * WPG + w];
-                C[cbatch + r] = f16_bits(v * p.alpha);
+                for (int nv = 0; nv < NV; ++nv) {
+                    float v = part[(q * NV + nv) * WPG];
+#pragma unroll
+                    for (int w = 1; w < WPG; ++w)
+                        v += part[(q * NV + nv) * WPG + w];
+                    C[cbatch + nv * p.c_vec + r] = f16_bits(v * p.alpha);
+                }
             }
         }
         return;
@@ -649,6 +700,7 @@ struct Plan {
     int wide_plain;
     int bfirst;           // b's inputs before the first ring of A (few row rounds per workgroup)
     int ilv;              // deferred rounds finished one per following round
+    int nv;               // right-hand vectors (1 for the GEMV)
     int64_t n_wg;
     int lds_bytes;
     size_t ws_partials;   // bytes of float32 partials (after the ticket region)
@@ -701,9 +753,10 @@ nvfp4_status_t check_shape(int64_t M, int64_t K, int64_t L)
     return NVFP4_OK;
 }
 
-Plan make_plan(int64_t M, int64_t K, int64_t L)
+Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
 {
     Plan pl{};
+    pl.nv = nv;
     const int64_t nchunks = K / 32;
     // slots holding at least one row: full 128-row blocks have 32, the last one min(32, M % 128)
     pl.ns = (int)(32 * (M / 128) + std::min<int64_t>(32, M % 128));
@@ -752,8 +805,9 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
     const int wpg = pl.lpr > 64 ? pl.lpr / 64 : 1;
     pl.stage_bytes = stage_bytes(pl.lpr, spw);
     // staged SFA, staged B, staged blocked SFB, per-wave row sums
-    pl.lds_bytes = (int)(pl.stage_bytes + (kStageB ? align_up((size_t)(64 * pl.lpr), kDmaBytes) : 0) +
-                         align_up((size_t)(32 * pl.lpr), kDmaBytes) + 4 * spw * wpg * (int)sizeof(float));
+    pl.lds_bytes = (int)(pl.stage_bytes + nv * (kStageB ? align_up((size_t)(64 * pl.lpr), kDmaBytes) : 0) +
+                         nv * align_up((size_t)(32 * pl.lpr), kDmaBytes) +
+                         4 * spw * wpg * nv * (int)sizeof(float));
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
     // row rounds of a full workgroup: 4*spw rows, kThreads/lpr rows per round
     pl.bfirst = cdiv(4 * spw * pl.lpr, kThreads) <= kBFirstMaxRounds ? 1 : 0;
@@ -767,52 +821,55 @@ Plan make_plan(int64_t M, int64_t K, int64_t L)
 
 thread_local int g_last_hip_error = 0;
 
-template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST, bool ILV>
+template <int LAYOUT, int LPR, bool SPLIT, bool BFIRST, bool ILV, int NV>
 hipError_t launch_kernel(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                          void *c, const Params &p, hipStream_t st)
 {
     const dim3 grid((uint32_t)pl.n_wg), block(kBlock);
-    hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, SPLIT, BFIRST, ILV>), grid, block, pl.lds_bytes, st,
+    hipLaunchKernelGGL((nvfp4_gemv_kernel<LAYOUT, LPR, SPLIT, BFIRST, ILV, NV>), grid, block, pl.lds_bytes, st,
                        (const uint8_t *)a, (uint32_t)pl.n_wg, p.M, p.K, p.L, p.spw, p.ns, p.kc_split,
                        p.a_row, p.a_extent, p.P, p.stage_bytes, (const uint8_t *)b, (const uint8_t *)sfa,
                        (const uint8_t *)sfb, (uint16_t *)c, p);
     return hipGetLastError();
 }
 
-template <int LAYOUT, int LPR, bool SPLIT>
+template <int LAYOUT, int LPR, bool SPLIT, int NV>
 hipError_t launch_split(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                         void *c, const Params &p, hipStream_t st)
 {
     if constexpr (LPR <= 64) {                             // the plan sets ilv only there, never with bfirst
         if (pl.ilv)
-            return launch_kernel<LAYOUT, LPR, SPLIT, false, true>(pl, a, b, sfa, sfb, c, p, st);
+            return launch_kernel<LAYOUT, LPR, SPLIT, false, true, NV>(pl, a, b, sfa, sfb, c, p, st);
     }
-    return pl.bfirst ? launch_kernel<LAYOUT, LPR, SPLIT, true, false>(pl, a, b, sfa, sfb, c, p, st)
-                     : launch_kernel<LAYOUT, LPR, SPLIT, false, false>(pl, a, b, sfa, sfb, c, p, st);
+    return pl.bfirst ? launch_kernel<LAYOUT, LPR, SPLIT, true, false, NV>(pl, a, b, sfa, sfb, c, p, st)
+                     : launch_kernel<LAYOUT, LPR, SPLIT, false, false, NV>(pl, a, b, sfa, sfb, c, p, st);
 }
 
-template <int LAYOUT, int LPR>
+template <int LAYOUT, int LPR, int NV>
 hipError_t launch_lpr(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                       void *c, const Params &p, hipStream_t st)
 {
-    return pl.S > 1 ? launch_split<LAYOUT, LPR, true>(pl, a, b, sfa, sfb, c, p, st)
-                    : launch_split<LAYOUT, LPR, false>(pl, a, b, sfa, sfb, c, p, st);
+    if constexpr (NV == 1) {                               // several vectors never split K
+        if (pl.S > 1)
+            return launch_split<LAYOUT, LPR, true, NV>(pl, a, b, sfa, sfb, c, p, st);
+    }
+    return launch_split<LAYOUT, LPR, false, NV>(pl, a, b, sfa, sfb, c, p, st);
 }
 
-template <int LAYOUT>
+template <int LAYOUT, int NV>
 hipError_t launch_layout(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
                          void *c, const Params &p, hipStream_t st)
 {
     switch (pl.lpr) {
-    case 256: return launch_lpr<LAYOUT, 256>(pl, a, b, sfa, sfb, c, p, st);
-    case 128: return launch_lpr<LAYOUT, 128>(pl, a, b, sfa, sfb, c, p, st);
-    case 64: return launch_lpr<LAYOUT, 64>(pl, a, b, sfa, sfb, c, p, st);
-    case 32: return launch_lpr<LAYOUT, 32>(pl, a, b, sfa, sfb, c, p, st);
-    case 16: return launch_lpr<LAYOUT, 16>(pl, a, b, sfa, sfb, c, p, st);
-    case 8: return launch_lpr<LAYOUT, 8>(pl, a, b, sfa, sfb, c, p, st);
-    case 4: return launch_lpr<LAYOUT, 4>(pl, a, b, sfa, sfb, c, p, st);
-    case 2: return launch_lpr<LAYOUT, 2>(pl, a, b, sfa, sfb, c, p, st);
-    default: return launch_lpr<LAYOUT, 1>(pl, a, b, sfa, sfb, c, p, st);
+    case 256: return launch_lpr<LAYOUT, 256, NV>(pl, a, b, sfa, sfb, c, p, st);
+    case 128: return launch_lpr<LAYOUT, 128, NV>(pl, a, b, sfa, sfb, c, p, st);
+    case 64: return launch_lpr<LAYOUT, 64, NV>(pl, a, b, sfa, sfb, c, p, st);
+    case 32: return launch_lpr<LAYOUT, 32, NV>(pl, a, b, sfa, sfb, c, p, st);
+    case 16: return launch_lpr<LAYOUT, 16, NV>(pl, a, b, sfa, sfb, c, p, st);
+    case 8: return launch_lpr<LAYOUT, 8, NV>(pl, a, b, sfa, sfb, c, p, st);
+    case 4: return launch_lpr<LAYOUT, 4, NV>(pl, a, b, sfa, sfb, c, p, st);
+    case 2: return launch_lpr<LAYOUT, 2, NV>(pl, a, b, sfa, sfb, c, p, st);
+    default: return launch_lpr<LAYOUT, 1, NV>(pl, a, b, sfa, sfb, c, p, st);
     }
 }
 
@@ -897,9 +954,19 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
         p.counters = (uint32_t *)ws;
         p.partials = (float *)((char *)ws + kCounterBytes);
     }
-    hipError_t e = sf_layout == NVFP4_SF_PLAIN
-                       ? launch_layout<NVFP4_SF_PLAIN>(pl, a, b, sfa, sfb, c, p, st)
-                       : launch_layout<NVFP4_SF_BLOCKED>(pl, a, b, sfa, sfb, c, p, st);
+    hipError_t e;
+    if (pl.nv == 2) {
+        // two vectors, dense: B [L][2][K/2], SFB per vector a row (plain) or
+        // the next 16-byte line of each tile (blocked), C [L][2][M]
+        p.b_vec = K / 2;
+        p.sfb_vec = sf_layout == NVFP4_SF_PLAIN ? K / 16 : 16;
+        p.c_vec = M;
+        e = sf_layout == NVFP4_SF_PLAIN ? launch_layout<NVFP4_SF_PLAIN, 2>(pl, a, b, sfa, sfb, c, p, st)
+                                        : launch_layout<NVFP4_SF_BLOCKED, 2>(pl, a, b, sfa, sfb, c, p, st);
+    } else {
+        e = sf_layout == NVFP4_SF_PLAIN ? launch_layout<NVFP4_SF_PLAIN, 1>(pl, a, b, sfa, sfb, c, p, st)
+                                        : launch_layout<NVFP4_SF_BLOCKED, 1>(pl, a, b, sfa, sfb, c, p, st);
+    }
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
         return NVFP4_ERR_HIP;
@@ -956,6 +1023,30 @@ nvfp4_status_t device_workspace(size_t need, void **out)
 }
 
 } // namespace
+
+// Two right-hand vectors through the GEMV kernel (A streamed and decoded once),
+// for the skinny GEMM with N = 2; dense operands laid out as nvfp4_gemm_small_n
+// takes them. Shapes that would need a K-split return NVFP4_ERR_INVALID_SHAPE
+// with nothing launched (the caller then uses its own kernel).
+nvfp4_status_t nvfp4_gemv_two_vectors(const void *a, const void *b, const void *sfa, const void *sfb, void *c,
+                                      int64_t M, int64_t K, int64_t L, int sf_layout, float alpha,
+                                      void *stream)
+{
+    nvfp4_status_t st = validate(a, b, sfa, sfb, c, M, K, L, sf_layout);
+    if (st != NVFP4_OK)
+        return st;
+    if (!std::isfinite(alpha))
+        return NVFP4_ERR_INVALID_SCALE;
+    const Plan pl = make_plan(M, K, L, 2);
+    if (pl.S > 1 || L * 2 * M > INT32_MAX / 2)
+        return NVFP4_ERR_INVALID_SHAPE;
+    nvfp4_strides_t sd = dense_strides(M, K, L, sf_layout);
+    sd.b_batch = K;                                        // two packed vectors per batch
+    if (sf_layout == NVFP4_SF_PLAIN)
+        sd.sfb_batch = 2 * (K / 16);                       // blocked: both rows sit in one 128-row block
+    sd.c_batch = 2 * M;
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, pl, sd, nullptr, (hipStream_t)stream);
+}
 
 extern "C" {
 

@@ -210,9 +210,9 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
  * Requirements and alignment as for nvfp4_gemv, 1 <= N <= 8, alpha finite.
  * Accumulation is float32 per row and vector (summation order the library's
  * own); no K-split and no workspace: small M*L leaves the GPU partly idle.
- * N = 1 runs the GEMV kernel (nvfp4_gemv_scaled) whenever the GEMV's plan
- * needs no split-K workspace, else this kernel; either way nothing is
- * allocated.
+ * N = 1 runs the GEMV kernel (nvfp4_gemv_scaled), and N = 2 the GEMV kernel
+ * with two vectors, whenever the GEMV's plan needs no split-K workspace; else
+ * the skinny kernel. Either way nothing is allocated.
  */
 nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa, const void *sfb,
                                   void *c, int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout,

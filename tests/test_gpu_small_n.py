@@ -43,7 +43,10 @@ def run_small_n(a, b, sfa, sfb, M, N, K, L, layout, alpha=1.0):
 
 
 CASES = [(1, 1, 32, 1), (7, 3, 96, 2), (128, 2, 2048, 1), (300, 4, 20480, 2), (1000, 8, 4096, 3),
-         (7168, 8, 2048, 1), (129, 5, 16384, 1), (4096, 2, 7168, 2), (64, 7, 65536, 1)]
+         (7168, 8, 2048, 1), (129, 5, 16384, 1), (4096, 2, 7168, 2), (64, 7, 65536, 1),
+         # N = 2 through the GEMV kernel (ragged M, several batches, segmented K),
+         # and N = 2 where a K-split is needed (the skinny kernel)
+         (1000, 2, 4096, 3), (300, 2, 20480, 2), (127, 2, 16384, 1)]
 
 
 @pytest.mark.parametrize("M,N,K,L", CASES)
@@ -59,8 +62,9 @@ def test_small_n_parity(M, N, K, L):
     assert np.array_equal(outs["plain"], outs["blocked"])
 
 
-def test_small_n_alpha_and_edge_codes():
-    M, N, K, L = 1000, 4, 4096, 2
+@pytest.mark.parametrize("N", [4, 2])
+def test_small_n_alpha_and_edge_codes(N):
+    M, K, L = 1000, 4096, 2
     inp = [synth.random_inputs(M, K, L, seed=60 + n, dist="edge") for n in range(N)]
     a = inp[0].a
     b = np.stack([x.b.reshape(L, K // 2) for x in inp], axis=1)

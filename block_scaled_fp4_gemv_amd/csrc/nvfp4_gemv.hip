@@ -287,8 +287,11 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     // chunk c of the group (2 scales) at +2 (c & 1); plain: the 2 scales of
     // (row q, chunk c) at (q * nck + c) * 2. Both roles pass the same barriers:
     // per segment one after the previous segment's staged bytes are read (not
-    // before the first), (blocked) one after b's inputs are staged and one
-    // that publishes the staged scales of A; then the ones of the epilogue.
+    // before the first), (blocked, BFIRST) one after the copies of b's inputs
+    // are issued, (blocked) one after b's inputs are staged, and one that
+    // publishes the staged scales of A; then the ones of the epilogue. With
+    // NV vectors, B and the SFB lines are staged per vector (B at
+    // b_stage + v*BSTB, SFB at sfb_stage + v*SFBB).
     if (loader) {
         // raised issue priority: its copies gate the publish barrier, and the
         // computing waves' A loads would otherwise take every free issue slot

@@ -110,7 +110,9 @@ __global__ __launch_bounds__(kRbThreads) void nvfp4_reblock_kernel(const uint8_t
             v.y = tile_words[(r32 + 32) * kLdsPitch + tl];
             v.z = tile_words[(r32 + 64) * kLdsPitch + tl];
             v.w = tile_words[(r32 + 96) * kLdsPitch + tl];
-            *(uint4_t *)(out + ((int64_t)rb * p.ncb + cb0 + tl) * 512 + r32 * 16) = v;
+            // written once and not read back here: non-temporal (measured
+            // 4-13% faster than plain stores; non-temporal loads were slower)
+            __builtin_nontemporal_store(v, (uint4_t *)(out + ((int64_t)rb * p.ncb + cb0 + tl) * 512 + r32 * 16));
         }
     }
 }

@@ -17,6 +17,15 @@
 // block sums against each b'_n (v_dot2_f32_f16), applies the SFA pair, and
 // sums the wave's lanes with DPP; per-wave sums go to LDS and are added in a
 // fixed order at the end, then rounded once to float16.
+//
+// From N = 3 the product runs on the matrix cores instead: a' = e2m1(A) *
+// e4m3(SFA) and b' are both exact in float16 (an E2M1 value has two
+// significant bits, an E4M3 one four; |a'| <= 6 * 448 and the smallest
+// nonzero one is 2^-10, a float16 normal), so the block scales are applied
+// before the contraction and sum_k a' b' is a plain float16 matrix product with
+// float32 accumulation. One v_mfma_f32_16x16x32_f16 takes 16 rows of A by 16
+// vector slots (N used, the others zero) over 32 k; its cost does not depend
+// on N, where the dot-product kernel's grows with it.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -57,6 +66,171 @@ __device__ inline int64_t sn_pair_offset(int64_t r, int32_t c, int32_t nkb, int3
     if (LAYOUT == NVFP4_SF_PLAIN)
         return r * nkb + 2 * c;
     return ((r >> 7) * ncb + (c >> 1)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 1) * 2;
+}
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Matrix-core kernel. A wave owns kMfRT tiles of 16 rows and a contiguous
+// share of the K-steps (one step = 4 chunks, 128 k); the kMfWaves waves of a
+// workgroup split K between them and their partial tiles are added in LDS in
+// a fixed order. In a step, lane group g (lanes 16g .. 16g+15) takes chunk g:
+// lane i of the group holds 16 bytes of row i of each tile (the MFMA's A
+// operand, k split into four runs of 8) and the same chunk of vector i (its B
+// operand; zero for i >= N). The 16x16 result has lane L holding rows
+// 4 (L / 16) + j, j < 4, of vector slot L % 16.
+constexpr int kMfMinN = 3;                    // N from which the matrix-core kernel runs
+constexpr int kMfRT = 2;                      // 16-row tiles per wave
+constexpr int kMfWaves = 4;                   // waves per workgroup, splitting K
+constexpr int kMfThreads = 64 * kMfWaves;
+constexpr int kMfRing = 4;                    // K-steps of loads in flight per lane
+
+struct MfParams {
+    int32_t M, K, L, N;
+    int32_t P;                                // workgroups per batch
+    int64_t sfa_batch, sfb_batch;             // bytes per batch of SFA / SFB
+    float alpha;
+};
+
+template <int LAYOUT>
+__global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
+    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, MfParams p)
+{
+    __shared__ float4_t mf_part[kMfWaves][kMfRT][64];
+    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t tile = (int32_t)(lid % (uint32_t)p.P), l = (int32_t)(lid / (uint32_t)p.P);
+    const int32_t M = p.M, K = p.K, N = p.N;
+    const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
+    const int32_t nfull = nchunks >> 2;                               // steps with all 4 chunks inside K
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);        // wave-uniform: scalar loop bounds
+    const int grp = lane >> 4, i16 = lane & 15;
+    const int32_t r0 = tile * (16 * kMfRT);
+    const int32_t s_begin = (int32_t)((int64_t)wave * nfull / kMfWaves);
+    const int32_t s_end = (int32_t)((int64_t)(wave + 1) * nfull / kMfWaves);
+    const int64_t row_bytes = K >> 1;
+    // step s of chunk column grp: A and B move by 64 bytes, a scale pair by
+    // 8 bytes (plain) or two 512-byte tiles (blocked; the pair's place in the
+    // tile depends only on the chunk's parity, which is grp's)
+    constexpr int64_t kSfStep = LAYOUT == NVFP4_SF_PLAIN ? 8 : 1024;
+
+    int32_t rows[kMfRT];                      // this lane's row of each tile (clamped: every load is real)
+    const uint8_t *a_ptr[kMfRT], *sa_ptr[kMfRT];
+    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
+#pragma unroll
+    for (int t = 0; t < kMfRT; ++t) {
+        rows[t] = min(r0 + 16 * t + i16, M - 1);
+        a_ptr[t] = A + ((int64_t)l * M + rows[t]) * row_bytes + grp * 16;
+        sa_ptr[t] = sfa_l + sn_pair_offset<LAYOUT>(rows[t], grp, nkb, ncb);
+    }
+    const int32_t n = min(i16, N - 1);
+    const bool n_live = i16 < N;
+    const uint8_t *b_row = B + ((int64_t)l * N + n) * row_bytes;
+    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+    const uint8_t *b_ptr = b_row + grp * 16;
+    const uint8_t *sb_ptr = sfb_l + sn_pair_offset<LAYOUT>(n, grp, nkb, ncb);
+
+    float4_t acc[kMfRT];
+#pragma unroll
+    for (int t = 0; t < kMfRT; ++t)
+        acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // one step: a' of each tile and b' from the codes and scale pairs (a
+    // vector slot past N gets a zero scale pair, so b' = 0 exactly), then
+    // four MFMAs per tile over the chunk's four runs of 8 k
+    auto mma_step = [&](const uint4_t (&araw)[kMfRT], const uint32_t (&sa)[kMfRT], uint4_t braw, uint32_t sb) {
+        uint4_t bp[4];
+        make_bprime(braw, sb, bp);
+#pragma unroll
+        for (int t = 0; t < kMfRT; ++t) {
+            uint4_t ap[4];
+            make_bprime(araw[t], sa[t], ap);                           // a' = e2m1(A) e4m3(SFA), exact
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap[q]),
+                                                                __builtin_bit_cast(half8_t, bp[q]), acc[t], 0, 0,
+                                                                0);
+        }
+    };
+
+    if (s_begin < s_end) {
+        uint4_t abuf[kMfRing][kMfRT], bbuf[kMfRing];
+        uint32_t sabuf[kMfRing][kMfRT], sbbuf[kMfRing];
+        // loads of step s into a ring slot; every step index is clamped into
+        // [s_begin, s_end), so the ring's refills past the end re-read the last step
+        auto load_step = [&](int32_t s, int slot) {
+            const int64_t ao = (int64_t)s * 64, so = (int64_t)s * kSfStep;
+#pragma unroll
+            for (int t = 0; t < kMfRT; ++t) {
+                abuf[slot][t] = __builtin_nontemporal_load((const uint4_t *)(a_ptr[t] + ao));
+                sabuf[slot][t] = *(const uint16_t *)(sa_ptr[t] + so);
+            }
+            bbuf[slot] = *(const uint4_t *)(b_ptr + ao);
+            sbbuf[slot] = *(const uint16_t *)(sb_ptr + so);
+        };
+#pragma unroll
+        for (int d = 0; d < kMfRing; ++d) {
+            load_step(min(s_begin + d, s_end - 1), d);                 // in slot order, as in the loop
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // whole rings with unconditional refills (a branch per slot here made
+        // the compiler drain the loads at every back-edge), then the steps
+        // already in the ring, without refills
+        int32_t s0 = s_begin;
+        for (; s0 + kMfRing <= s_end; s0 += kMfRing) {
+#pragma unroll
+            for (int d = 0; d < kMfRing; ++d) {
+                // consume the slot, then refill it: its registers are reused
+                // in place (refilling before the decode kept two copies of
+                // the ring live and the compiler drained the loads every ring)
+                mma_step(abuf[d], sabuf[d], bbuf[d], n_live ? sbbuf[d] : 0u);
+                __builtin_amdgcn_sched_barrier(0);                     // keep the refill here, not
+                load_step(min(s0 + d + kMfRing, s_end - 1), d);       // sunk to the end of the ring
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < kMfRing; ++d)
+            if (s0 + d < s_end)
+                mma_step(abuf[d], sabuf[d], bbuf[d], n_live ? sbbuf[d] : 0u);
+    }
+
+    // the last step of a K that is not a multiple of 128: chunks past K (lane
+    // groups past the end) load a real chunk and get zero scale pairs, so they
+    // add exact zeros; taken by the last wave
+    if ((nchunks & 3) != 0 && wave == kMfWaves - 1) {
+        const int32_t c = min(4 * nfull + grp, nchunks - 1);
+        const bool live = 4 * nfull + grp < nchunks;
+        uint4_t araw[kMfRT];
+        uint32_t sa[kMfRT];
+#pragma unroll
+        for (int t = 0; t < kMfRT; ++t) {
+            araw[t] = __builtin_nontemporal_load(
+                (const uint4_t *)(A + ((int64_t)l * M + rows[t]) * row_bytes + (int64_t)c * 16));
+            const uint32_t v = *(const uint16_t *)(sfa_l + sn_pair_offset<LAYOUT>(rows[t], c, nkb, ncb));
+            sa[t] = live ? v : 0u;
+        }
+        const uint4_t braw = *(const uint4_t *)(b_row + (int64_t)c * 16);
+        const uint32_t v = *(const uint16_t *)(sfb_l + sn_pair_offset<LAYOUT>(n, c, nkb, ncb));
+        mma_step(araw, sa, braw, (live && n_live) ? v : 0u);
+    }
+
+#pragma unroll
+    for (int t = 0; t < kMfRT; ++t)
+        mf_part[wave][t][lane] = acc[t];
+    __syncthreads();
+    for (int e = tid; e < kMfRT * 64 * 4; e += kMfThreads) {
+        const int t = e >> 8, ln = (e >> 2) & 63, j = e & 3;
+        const int32_t col = ln & 15, row = r0 + 16 * t + 4 * (ln >> 4) + j;
+        if (col < N && row < M) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kMfWaves; ++w)
+                v += ((const float *)&mf_part[w][t][ln])[j];
+            C[((int64_t)l * N + col) * M + row] = f16_bits(v * p.alpha);
+        }
+    }
 }
 
 template <int LAYOUT, int N>
@@ -258,6 +432,16 @@ hipError_t sn_dispatch(int64_t N, int64_t grid, int lds, const void *a, const vo
     }
 }
 
+template <int LAYOUT>
+hipError_t mf_launch(int64_t grid, const void *a, const void *b, const void *sfa, const void *sfb, void *c,
+                     const MfParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL((nvfp4_gemm_small_n_mfma_kernel<LAYOUT>), dim3((uint32_t)grid), dim3(kMfThreads), 0, st,
+                       (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa, (const uint8_t *)sfb,
+                       (uint16_t *)c, p);
+    return hipGetLastError();
+}
+
 bool sn_aligned(const void *q, uintptr_t a) { return ((uintptr_t)q & (a - 1)) == 0; }
 
 } // namespace
@@ -270,6 +454,19 @@ nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t 
     if (M < 1 || N < 1 || N > kSnMaxN || L < 1 || K < 32 || K % 32 != 0 || K > (INT64_C(1) << 22) ||
         M > INT32_MAX / 2 || L > INT32_MAX / 2 || L * M > (INT64_C(1) << 62) / K)
         return NVFP4_ERR_INVALID_SHAPE;
+    if (N >= kMfMinN) {
+        // the matrix-core kernel: one workgroup per kMfRT tiles of 16 rows, static LDS only
+        const int64_t rows = 16 * kMfRT, P = (M + rows - 1) / rows;
+        if (L * P > INT32_MAX)
+            return NVFP4_ERR_INVALID_SHAPE;
+        if (rows_per_wg)
+            *rows_per_wg = (int32_t)std::min<int64_t>(rows, M);
+        if (workgroups)
+            *workgroups = L * P;
+        if (lds_bytes)
+            *lds_bytes = 0;
+        return NVFP4_OK;
+    }
     // about the target number of workgroups, each a contiguous row range of one batch,
     // with the per-wave row sums inside the LDS budget
     const int64_t rmax = kSnPartBudget / (N * kSnWaves * (int64_t)sizeof(float));
@@ -319,25 +516,37 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
         if (st2 != NVFP4_ERR_INVALID_SHAPE)
             return st2;
     }
-    SnParams p{};
-    p.M = (int32_t)M;
-    p.K = (int32_t)K;
-    p.L = (int32_t)L;
-    p.R = R;
-    p.P = (int32_t)(grid / L);
-    p.alpha = alpha;
     const int64_t nkb = K / 16, ncb = (nkb + 3) / 4;
-    if (sf_layout == NVFP4_SF_PLAIN) {
-        p.sfa_batch = M * nkb;
-        p.sfb_batch = N * nkb;
+    const int64_t sfa_batch = sf_layout == NVFP4_SF_PLAIN ? M * nkb : ((M + 127) / 128) * ncb * 512;
+    const int64_t sfb_batch = sf_layout == NVFP4_SF_PLAIN ? N * nkb : ((N + 127) / 128) * ncb * 512;
+    hipError_t e;
+    if (N >= kMfMinN) {
+        MfParams q{};
+        q.M = (int32_t)M;
+        q.K = (int32_t)K;
+        q.L = (int32_t)L;
+        q.N = (int32_t)N;
+        q.P = (int32_t)(grid / L);
+        q.sfa_batch = sfa_batch;
+        q.sfb_batch = sfb_batch;
+        q.alpha = alpha;
+        e = sf_layout == NVFP4_SF_PLAIN
+                ? mf_launch<NVFP4_SF_PLAIN>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream)
+                : mf_launch<NVFP4_SF_BLOCKED>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream);
     } else {
-        p.sfa_batch = ((M + 127) / 128) * ncb * 512;
-        p.sfb_batch = ((N + 127) / 128) * ncb * 512;
+        SnParams p{};
+        p.M = (int32_t)M;
+        p.K = (int32_t)K;
+        p.L = (int32_t)L;
+        p.R = R;
+        p.P = (int32_t)(grid / L);
+        p.alpha = alpha;
+        p.sfa_batch = sfa_batch;
+        p.sfb_batch = sfb_batch;
+        e = sf_layout == NVFP4_SF_PLAIN
+                ? sn_dispatch<NVFP4_SF_PLAIN>(N, grid, lds, a, b, sfa, sfb, c, p, (hipStream_t)stream)
+                : sn_dispatch<NVFP4_SF_BLOCKED>(N, grid, lds, a, b, sfa, sfb, c, p, (hipStream_t)stream);
     }
-    const hipError_t e = sf_layout == NVFP4_SF_PLAIN
-                             ? sn_dispatch<NVFP4_SF_PLAIN>(N, grid, lds, a, b, sfa, sfb, c, p, (hipStream_t)stream)
-                             : sn_dispatch<NVFP4_SF_BLOCKED>(N, grid, lds, a, b, sfa, sfb, c, p,
-                                                             (hipStream_t)stream);
     if (e != hipSuccess) {
         nvfp4_record_hip_error((int)e);
         return NVFP4_ERR_HIP;

@@ -264,13 +264,16 @@ def test_small_n_validation():
 
 
 def test_small_n_plan():
-    # one workgroup per CU for N <= 2, two from N = 3 (latency of the lane reductions)
+    # N <= 2: the dot-product kernel, one workgroup per CU
     p = g.nvfp4_gemm_small_n_plan(7168, 2, 16384, 1)
     assert p["workgroups"] == 256 and p["rows_per_wg"] == 28
-    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1)
-    assert p["workgroups"] == 512 and p["rows_per_wg"] == 14
-    p = g.nvfp4_gemm_small_n_plan(100000, 8, 64, 1)
+    p = g.nvfp4_gemm_small_n_plan(100000, 2, 64, 1)
     assert p["lds_bytes"] <= 48 * 1024
+    # N >= 3: the matrix-core kernel, 32-row tiles per workgroup, static LDS only
+    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1)
+    assert p["workgroups"] == 224 and p["rows_per_wg"] == 32 and p["lds_bytes"] == 0
+    p = g.nvfp4_gemm_small_n_plan(7, 3, 96, 2)
+    assert p["workgroups"] == 2 and p["rows_per_wg"] == 7
     with pytest.raises(g.Nvfp4Error):
         g.nvfp4_gemm_small_n_plan(128, 9, 256, 1)
 

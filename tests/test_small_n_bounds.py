@@ -1,6 +1,8 @@
-"""CPU mirror of nvfp4_gemm_small_n's index arithmetic over its whole grid
-(keep in step with nvfp4_gemm_small_n.hip: 256 lanes, one chunk per lane per
-256-chunk segment, a ring of 8 rows): every A, B, SFA and SFB read is inside
+"""CPU mirror of the index arithmetic of nvfp4_gemm_small_n's dot-product
+kernel (N <= 2; from N = 3 the matrix-core kernel runs, mirrored in
+test_small_n_mfma_bounds.py) over its whole grid (keep in step with
+nvfp4_gemm_small_n.hip: 256 lanes, one chunk per lane per 256-chunk segment,
+a ring of 8 rows): every A, B, SFA and SFB read is inside
 its tensor, the per-wave row sums stay inside the planned LDS, and every
 output (l, n, m) is written exactly once."""
 import numpy as np
@@ -66,9 +68,9 @@ def check(M, N, K, L, layout):
     assert np.all(written == 1)
 
 
-@pytest.mark.parametrize("M,N,K,L", [(1, 1, 32, 1), (7, 3, 96, 2), (128, 8, 2048, 1), (300, 2, 20480, 2),
-                                     (1000, 4, 4096, 3), (7168, 8, 2048, 1), (4096, 5, 7168, 8),
-                                     (129, 7, 16384, 1), (100000, 8, 64, 1)])
+@pytest.mark.parametrize("M,N,K,L", [(1, 1, 32, 1), (7, 2, 96, 2), (128, 1, 2048, 1), (300, 2, 20480, 2),
+                                     (1000, 2, 4096, 3), (7168, 2, 2048, 1), (4096, 1, 7168, 8),
+                                     (129, 2, 16384, 1), (100000, 2, 64, 1)])
 @pytest.mark.parametrize("layout", [0, 1])
 def test_small_n_addresses(M, N, K, L, layout):
     check(M, N, K, L, layout)

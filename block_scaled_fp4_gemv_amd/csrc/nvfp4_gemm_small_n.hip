@@ -1,5 +1,6 @@
 // NVFP4 block-scaled skinny GEMM for a few right-hand vectors (N = 1..8) on
-// MI355X (gfx950).
+// MI355X (gfx950): a dot-product kernel for N <= 2 and a matrix-core kernel
+// from N = 3.
 //
 // c[l][n][m] = fp16( alpha * sum_k e2m1(A[l][m][k]) e4m3(SFA[l][m][k/16])
 //                                 * e2m1(B[l][n][k]) e4m3(SFB[l][n][k/16]) )
@@ -8,7 +9,8 @@
 // its N = 1 column. A is streamed once for all N vectors, so each chunk of A
 // is decoded once and dotted with N vectors of b'.
 //
-// Work split. A workgroup (4 waves, 256 lanes) owns a contiguous range of R
+// Dot-product kernel (N <= 2, where the GEMV kernel is not used). A workgroup
+// (4 waves, 256 lanes) owns a contiguous range of R
 // rows of one batch. Lane j owns chunk c0 + j of every K-segment of 256
 // chunks (8192 k) and keeps b'_n = e2m1(B_n) * e4m3(SFB_n) of that chunk for
 // all N vectors in registers (16 VGPRs each, exact float16). It walks the
@@ -43,12 +45,9 @@ constexpr int kSnWaves = kSnThreads / 64;
 constexpr int kSnRing = 8;                    // rows of A in flight per lane
 constexpr int kSnMaxN = 8;
 constexpr int kSnPartBudget = 48 * 1024;      // LDS bytes of per-wave row sums
-// Workgroups to aim for: one per CU for N <= 2; two per CU from N = 3, where
-// the per-row lane reductions (dependent DPP chains) need a second wave per
-// SIMD to hide their latency (headline A, N = 4 / 8: 40.9 -> 35.7 / 68.8 ->
-// 54.0 us; N = 2: 27.8 -> 30.9, so it keeps one).
-constexpr int64_t kSnTargetWGsFew = 256;
-constexpr int64_t kSnTargetWGsMany = 512;
+// Workgroups to aim for: one per CU (N = 2 on the headline A: 27.8 us with
+// one, 30.9 with two).
+constexpr int64_t kSnTargetWGs = 256;
 
 struct SnParams {
     int32_t M, K, L;
@@ -282,112 +281,65 @@ __global__ __launch_bounds__(kSnThreads) void nvfp4_gemm_small_n_kernel(
             make_bprime(braw, sb, bp[n]);
         }
 
-        // N <= 4: the lane sums of a whole ring come after its dot products, as
-        // independent DPP chains (N = 2: 27.8 -> 25.5 us on the headline A). With
-        // more vectors the extra live values cost more than they hide.
-        if constexpr (N <= 4) {
-            for (int32_t i0 = 0; i0 < nr; i0 += kSnRing) {
-                // per row of the ring: decode once, dot with every vector, refill;
-                // the lane sums of all kSnRing * N (row, vector) values come after,
-                // as independent DPP chains the scheduler can interleave
-                float vr[kSnRing][N];
+        // the lane sums of a whole ring come after its dot products, as
+        // independent DPP chains (N = 2: 27.8 -> 25.5 us on the headline A)
+        for (int32_t i0 = 0; i0 < nr; i0 += kSnRing) {
+            // per row of the ring: decode once, dot with every vector, refill;
+            // the lane sums of all kSnRing * N (row, vector) values come after,
+            // as independent DPP chains the scheduler can interleave
+            float vr[kSnRing][N];
 #pragma unroll
-                for (int d = 0; d < kSnRing; ++d) {
-                    const int32_t i = i0 + d;
-                    const uint4_t a = abuf[d];
-                    const uint32_t s = sbuf[d];
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_row(i + kSnRing, abuf[d], sbuf[d]);              // refill after the last use
-                    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-                    half2_t h[16];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        h[4 * q + 0] = fp4x2<0>(w[q]);
-                        h[4 * q + 1] = fp4x2<1>(w[q]);
-                        h[4 * q + 2] = fp4x2<2>(w[q]);
-                        h[4 * q + 3] = fp4x2<3>(w[q]);
-                    }
-                    const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(s, false);
-#pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            const uint4_t bl = bp[n][q], bh = bp[n][2 + q];
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 0], as_h2(bl.x), lo, false);
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 1], as_h2(bl.y), lo, false);
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 2], as_h2(bl.z), lo, false);
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 3], as_h2(bl.w), lo, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 0], as_h2(bh.x), hi, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 1], as_h2(bh.y), hi, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 2], as_h2(bh.z), hi, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 3], as_h2(bh.w), hi, false);
-                        }
-                        const float v = __builtin_fmaf(hi, sf.y, lo * sf.x);
-                        vr[d][n] = live ? v : 0.0f;
-                    }
-                }
+            for (int d = 0; d < kSnRing; ++d) {
+                const int32_t i = i0 + d;
+                const uint4_t a = abuf[d];
+                const uint32_t s = sbuf[d];
                 __builtin_amdgcn_sched_barrier(0);
+                load_row(i + kSnRing, abuf[d], sbuf[d]);              // refill after the last use
+                const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+                half2_t h[16];
 #pragma unroll
-                for (int d = 0; d < kSnRing; ++d) {
-#pragma unroll
-                    for (int n = 0; n < N; ++n)
-                        vr[d][n] = group_sum<64>(vr[d][n]);
+                for (int q = 0; q < 4; ++q) {
+                    h[4 * q + 0] = fp4x2<0>(w[q]);
+                    h[4 * q + 1] = fp4x2<1>(w[q]);
+                    h[4 * q + 2] = fp4x2<2>(w[q]);
+                    h[4 * q + 3] = fp4x2<3>(w[q]);
                 }
-                if (lane == 63) {
+                const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(s, false);
 #pragma unroll
-                    for (int d = 0; d < kSnRing; ++d) {
-                        const int32_t i = i0 + d;
-                        if (i < nr) {
+                for (int n = 0; n < N; ++n) {
+                    float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-                            for (int n = 0; n < N; ++n) {
-                                float *dst = sn_part + ((int64_t)i * N + n) * kSnWaves + wave;
-                                *dst = first_seg ? vr[d][n] : *dst + vr[d][n];
-                            }
-                        }
+                    for (int q = 0; q < 2; ++q) {
+                        const uint4_t bl = bp[n][q], bh = bp[n][2 + q];
+                        lo = __builtin_amdgcn_fdot2(h[4 * q + 0], as_h2(bl.x), lo, false);
+                        lo = __builtin_amdgcn_fdot2(h[4 * q + 1], as_h2(bl.y), lo, false);
+                        lo = __builtin_amdgcn_fdot2(h[4 * q + 2], as_h2(bl.z), lo, false);
+                        lo = __builtin_amdgcn_fdot2(h[4 * q + 3], as_h2(bl.w), lo, false);
+                        hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 0], as_h2(bh.x), hi, false);
+                        hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 1], as_h2(bh.y), hi, false);
+                        hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 2], as_h2(bh.z), hi, false);
+                        hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 3], as_h2(bh.w), hi, false);
                     }
+                    const float v = __builtin_fmaf(hi, sf.y, lo * sf.x);
+                    vr[d][n] = live ? v : 0.0f;
                 }
             }
-        } else {
-            for (int32_t i0 = 0; i0 < nr; i0 += kSnRing) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < kSnRing; ++d) {
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    vr[d][n] = group_sum<64>(vr[d][n]);
+            }
+            if (lane == 63) {
 #pragma unroll
                 for (int d = 0; d < kSnRing; ++d) {
                     const int32_t i = i0 + d;
-                    const uint4_t a = abuf[d];
-                    const uint32_t s = sbuf[d];
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_row(i + kSnRing, abuf[d], sbuf[d]);              // refill after the last use
-                    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-                    half2_t h[16];
+                    if (i < nr) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        h[4 * q + 0] = fp4x2<0>(w[q]);
-                        h[4 * q + 1] = fp4x2<1>(w[q]);
-                        h[4 * q + 2] = fp4x2<2>(w[q]);
-                        h[4 * q + 3] = fp4x2<3>(w[q]);
-                    }
-                    const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(s, false);
-#pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            const uint4_t bl = bp[n][q], bh = bp[n][2 + q];
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 0], as_h2(bl.x), lo, false);
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 1], as_h2(bl.y), lo, false);
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 2], as_h2(bl.z), lo, false);
-                            lo = __builtin_amdgcn_fdot2(h[4 * q + 3], as_h2(bl.w), lo, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 0], as_h2(bh.x), hi, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 1], as_h2(bh.y), hi, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 2], as_h2(bh.z), hi, false);
-                            hi = __builtin_amdgcn_fdot2(h[8 + 4 * q + 3], as_h2(bh.w), hi, false);
-                        }
-                        float v = __builtin_fmaf(hi, sf.y, lo * sf.x);
-                        v = live ? v : 0.0f;
-                        v = group_sum<64>(v);
-                        if (lane == 63 && i < nr) {
+                        for (int n = 0; n < N; ++n) {
                             float *dst = sn_part + ((int64_t)i * N + n) * kSnWaves + wave;
-                            *dst = first_seg ? v : *dst + v;
+                            *dst = first_seg ? vr[d][n] : *dst + vr[d][n];
                         }
                     }
                 }
@@ -420,16 +372,10 @@ template <int LAYOUT>
 hipError_t sn_dispatch(int64_t N, int64_t grid, int lds, const void *a, const void *b, const void *sfa,
                        const void *sfb, void *c, const SnParams &p, hipStream_t st)
 {
-    switch (N) {
-    case 1: return sn_launch<LAYOUT, 1>(grid, lds, a, b, sfa, sfb, c, p, st);
-    case 2: return sn_launch<LAYOUT, 2>(grid, lds, a, b, sfa, sfb, c, p, st);
-    case 3: return sn_launch<LAYOUT, 3>(grid, lds, a, b, sfa, sfb, c, p, st);
-    case 4: return sn_launch<LAYOUT, 4>(grid, lds, a, b, sfa, sfb, c, p, st);
-    case 5: return sn_launch<LAYOUT, 5>(grid, lds, a, b, sfa, sfb, c, p, st);
-    case 6: return sn_launch<LAYOUT, 6>(grid, lds, a, b, sfa, sfb, c, p, st);
-    case 7: return sn_launch<LAYOUT, 7>(grid, lds, a, b, sfa, sfb, c, p, st);
-    default: return sn_launch<LAYOUT, 8>(grid, lds, a, b, sfa, sfb, c, p, st);
-    }
+    // N >= kMfMinN runs the matrix-core kernel
+    static_assert(kMfMinN == 3, "the dot-product kernel is instantiated for N = 1, 2");
+    return N == 1 ? sn_launch<LAYOUT, 1>(grid, lds, a, b, sfa, sfb, c, p, st)
+                  : sn_launch<LAYOUT, 2>(grid, lds, a, b, sfa, sfb, c, p, st);
 }
 
 template <int LAYOUT>
@@ -470,7 +416,7 @@ nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t 
     // about the target number of workgroups, each a contiguous row range of one batch,
     // with the per-wave row sums inside the LDS budget
     const int64_t rmax = kSnPartBudget / (N * kSnWaves * (int64_t)sizeof(float));
-    const int64_t target = N <= 2 ? kSnTargetWGsFew : kSnTargetWGsMany;
+    const int64_t target = kSnTargetWGs;
     int64_t P = std::min<int64_t>(M, std::max<int64_t>(1, target / L));
     P = std::max<int64_t>(P, (M + rmax - 1) / rmax);
     const int64_t R = (M + P - 1) / P;

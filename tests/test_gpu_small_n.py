@@ -46,7 +46,9 @@ CASES = [(1, 1, 32, 1), (7, 3, 96, 2), (128, 2, 2048, 1), (300, 4, 20480, 2), (1
          (7168, 8, 2048, 1), (129, 5, 16384, 1), (4096, 2, 7168, 2), (64, 7, 65536, 1),
          # N = 2 through the GEMV kernel (ragged M, several batches, segmented K),
          # and N = 2 where a K-split is needed (the skinny kernel)
-         (1000, 2, 4096, 3), (300, 2, 20480, 2), (127, 2, 16384, 1)]
+         (1000, 2, 4096, 3), (300, 2, 20480, 2), (127, 2, 16384, 1),
+         # matrix-core kernel over many batches, ragged M and K
+         (300, 4, 1056, 120), (100, 8, 160, 300)]
 
 
 @pytest.mark.parametrize("M,N,K,L", CASES)

@@ -79,7 +79,8 @@ def emulate(M, N, K, L, layout):
 
 
 @pytest.mark.parametrize("M,N,K,L", [(1, 3, 32, 1), (7, 3, 96, 2), (33, 8, 160, 1), (64, 4, 4096, 1),
-                                     (129, 5, 1056, 2), (300, 4, 20480, 1), (45, 7, 224, 3)])
+                                     (129, 5, 1056, 2), (300, 4, 20480, 1), (45, 7, 224, 3),
+                                     (100, 5, 160, 300), (300, 4, 1056, 120)])
 @pytest.mark.parametrize("layout", ["plain", "blocked"])
 def test_mfma_kernel_indexing(M, N, K, L, layout):
     taken, written = emulate(M, N, K, L, layout)

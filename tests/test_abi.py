@@ -9,11 +9,14 @@ import pytest
 
 import block_scaled_fp4_gemv_amd as g
 import synth
+from conftest import no_gpu_only
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4_gemv.h")
 
-A16 = 0x10000       # fake but aligned device addresses: validation never dereferences them
+A16 = 0x10000       # fake but aligned device addresses: validation never dereferences them.
+# A call whose arguments all pass validation would launch on them, so such
+# tests carry @no_gpu_only and skip wherever a GPU is visible.
 OK_ARGS = dict(a=A16, b=A16 + 0x100, sfa=A16 + 0x200, sfb=A16 + 0x300, c=A16 + 0x400)
 
 
@@ -60,6 +63,7 @@ def test_misaligned(ptr, off):
     assert call(**{ptr: OK_ARGS[ptr] + off}) == g.NVFP4_ERR_MISALIGNED
 
 
+@no_gpu_only
 def test_alignment_minimums_accepted_by_validation():
     # 4-byte aligned sfb and 2-byte aligned c pass validation (they then
     # fail later only because there is no GPU here, never with MISALIGNED)
@@ -242,6 +246,7 @@ def test_strided_null_strides_and_order():
     assert lib.nvfp4_gemv_strided(*bad, None, 1.0, None, 0, None) == g.NVFP4_ERR_INVALID_SHAPE
 
 
+@no_gpu_only
 def test_strided_cases_pass_validation():
     from test_kernel_bounds import STRIDED
     for M, K, L, layout, over in STRIDED:

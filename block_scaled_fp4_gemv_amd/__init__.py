@@ -38,6 +38,8 @@ NVFP4_ERR_INVALID_STRIDE = 8
 
 EXPORTED_SYMBOLS = (
     "nvfp4_gemv",
+    "nvfp4_gemv_noalloc",
+    "nvfp4_gemv_noalloc_scratch_bytes",
     "nvfp4_gemv_workspace_bytes",
     "nvfp4_gemv_ex",
     "nvfp4_gemv_scaled",
@@ -104,6 +106,10 @@ def lib():
     L.nvfp4_gemv.restype = i32
     L.nvfp4_gemv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.nvfp4_gemv_ex.restype = i32
+    L.nvfp4_gemv_noalloc.restype = i32
+    L.nvfp4_gemv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.nvfp4_gemv_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    L.nvfp4_gemv_noalloc_scratch_bytes.argtypes = []
     L.nvfp4_gemv_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
     L.nvfp4_gemv_scaled.restype = i32
     L.nvfp4_gemv_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.c_float, vp,
@@ -203,6 +209,21 @@ def nvfp4_gemv(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, stream=None
     st = lib().nvfp4_gemv(pa, pb, psa, psb, pc, M, K, L, lay, _stream_handle(stream))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemv")
+
+
+def nvfp4_gemv_noalloc(a, b, sfa, sfb, c, M: int, K: int, L: int, sf_layout, stream=None) -> None:
+    """As nvfp4_gemv, with the split-K workspace taken from the library's fixed
+    per-device scratch array (no allocation; calls on one GPU must not overlap)."""
+    (pa, na), (pb, nb), (psa, nsa), (psb, nsb), (pc, nc) = map(_ptr_and_bytes, (a, b, sfa, sfb, c))
+    lay = layout_id(sf_layout)
+    _check_sizes(M, K, L, lay, a=na, b=nb, sfa=nsa, sfb=nsb, c=nc)
+    st = lib().nvfp4_gemv_noalloc(pa, pb, psa, psb, pc, M, K, L, lay, _stream_handle(stream))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemv_noalloc")
+
+
+def nvfp4_gemv_noalloc_scratch_bytes() -> int:
+    return int(lib().nvfp4_gemv_noalloc_scratch_bytes())
 
 
 def nvfp4_gemv_workspace_bytes(M: int, K: int, L: int) -> int:

@@ -1025,6 +1025,60 @@ nvfp4_status_t device_workspace(size_t need, void **out)
     return NVFP4_OK;
 }
 
+// ------------------------------------------------ allocation-free split-K scratch
+// nvfp4_gemv_noalloc takes its split-K workspace (tickets, then float32
+// partials) from this file-scope device array instead of hipMalloc: one copy
+// per GPU the library runs on, held until the process ends. In host code the
+// name `scratch` is only a stand-in for the device symbol; host code uses the
+// address hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kScratchBytes = 64 * 1024;
+static_assert(kScratchBytes > kCounterBytes, "the ticket region fits the scratch array");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// zeroes n 32-bit words (the ticket region) once per device
+__global__ void zero_words_kernel(uint32_t *p, int n)
+{
+    for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x)
+        p[i] = 0u;
+}
+
+std::mutex g_scratch_mutex;
+std::vector<void *> g_scratch;    // per device: the scratch array's device address (nullptr: not set up)
+
+// The scratch array of the current device. Set-up (first call on a device):
+// its address, and one clear of the ticket region on `st` (a small kernel, not
+// a memset, so that it may be captured). Afterwards the tickets stay zero: the
+// last workgroup of every row range resets its ticket, and every partial is
+// written before it is read.
+nvfp4_status_t scratch_for_device(hipStream_t st, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return NVFP4_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if ((int)g_scratch.size() <= dev)
+        g_scratch.resize(dev + 1, nullptr);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess || !ptr) {
+            g_last_hip_error = (int)e;
+            return NVFP4_ERR_HIP;
+        }
+        hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, (uint32_t *)ptr,
+                           (int)(kCounterBytes / sizeof(uint32_t)));
+        if ((e = hipGetLastError()) != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return NVFP4_ERR_HIP;
+        }
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return NVFP4_OK;
+}
+
 } // namespace
 
 // Two right-hand vectors through the GEMV kernel (A streamed and decoded once),
@@ -1066,6 +1120,26 @@ nvfp4_status_t nvfp4_gemv(const void *a, const void *b, const void *sfa, const v
     return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, dense_strides(M, K, L, sf_layout), ws,
                   (hipStream_t)stream);
 }
+
+nvfp4_status_t nvfp4_gemv_noalloc(const void *a, const void *b, const void *sfa, const void *sfb, void *c,
+                                  int64_t M, int64_t K, int64_t L, int sf_layout, void *stream)
+{
+    nvfp4_status_t st = validate(a, b, sfa, sfb, c, M, K, L, sf_layout);
+    if (st != NVFP4_OK)
+        return st;
+    const Plan pl = make_plan(M, K, L);
+    void *ws = nullptr;
+    if (pl.ws_total > 0) {
+        if (pl.ws_total > kScratchBytes)
+            return NVFP4_ERR_WORKSPACE;                    // beyond the fixed scratch array
+        if ((st = scratch_for_device((hipStream_t)stream, &ws)) != NVFP4_OK)
+            return st;
+    }
+    return launch(a, b, sfa, sfb, c, M, K, L, sf_layout, 1.0f, pl, dense_strides(M, K, L, sf_layout), ws,
+                  (hipStream_t)stream);
+}
+
+size_t nvfp4_gemv_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 size_t nvfp4_gemv_workspace_bytes(int64_t M, int64_t K, int64_t L)
 {

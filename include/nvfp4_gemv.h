@@ -85,6 +85,28 @@ nvfp4_status_t nvfp4_gemv(const void *a, const void *b, const void *sfa, const v
                           void *stream);
 
 /*
+ * As nvfp4_gemv, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. It calls no
+ * hipMalloc, hipFree or allocating routine. The split-K workspace comes from a
+ * fixed scratch array of nvfp4_gemv_noalloc_scratch_bytes() bytes that the
+ * library holds in device memory, one copy per GPU it runs on, until the
+ * process ends. The first call on a device looks up that copy's address and
+ * enqueues one small kernel on `stream` that zeroes its ticket region; every
+ * completed call leaves the tickets zero again. All calls on one GPU share its
+ * copy, so calls that overlap in time on one GPU (two streams, or two host
+ * threads) race and must not be made. A shape whose workspace
+ * (nvfp4_gemv_workspace_bytes) exceeds the array returns NVFP4_ERR_WORKSPACE
+ * with nothing launched; the library's own plans split K only for small M*L,
+ * whose workspace stays far below it.
+ */
+nvfp4_status_t nvfp4_gemv_noalloc(const void *a, const void *b, const void *sfa, const void *sfb,
+                                  void *c, int64_t M, int64_t K, int64_t L, int sf_layout,
+                                  void *stream);
+
+/* Bytes of nvfp4_gemv_noalloc's fixed scratch array (the workspace limit). */
+size_t nvfp4_gemv_noalloc_scratch_bytes(void);
+
+/*
  * Workspace bytes nvfp4_gemv_ex needs for this shape (0 when the shape is not
  * split along K). The value depends only on M, K and L.
  */

@@ -292,3 +292,21 @@ def test_stream_read_validation():
         assert L.nvfp4_stream_read(A16, bad, A16, None) == g.NVFP4_ERR_INVALID_SHAPE, bad
     assert L.nvfp4_stream_read(A16 + 8, unit, A16, None) == g.NVFP4_ERR_MISALIGNED
     assert L.nvfp4_stream_read(A16, unit, A16 + 2, None) == g.NVFP4_ERR_MISALIGNED
+
+
+def test_noalloc_validation_before_launch():
+    lib = g.lib()
+    args = [OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"], OK_ARGS["c"], 128, 256, 1, 0, None]
+    bad = list(args)
+    bad[0] = None
+    assert lib.nvfp4_gemv_noalloc(*bad) == g.NVFP4_ERR_NULL_POINTER
+    bad = list(args)
+    bad[6] = 48
+    assert lib.nvfp4_gemv_noalloc(*bad) == g.NVFP4_ERR_INVALID_SHAPE
+    bad = list(args)
+    bad[4] = OK_ARGS["c"] + 1
+    assert lib.nvfp4_gemv_noalloc(*bad) == g.NVFP4_ERR_MISALIGNED
+    bad = list(args)
+    bad[8] = 7
+    assert lib.nvfp4_gemv_noalloc(*bad) == g.NVFP4_ERR_INVALID_LAYOUT
+    assert lib.nvfp4_gemv_noalloc_scratch_bytes() == 64 * 1024

@@ -9,19 +9,19 @@ synthetic and already resident in HBM; consecutive steps rotate through enough
 distinct sets (>= 512 MiB together) that neither the L2s nor the 256 MiB
 Infinity Cache hold the next step's operands.
 
-Timing:
-  * parity of input set 0 against the oracle comes first; then W warmup
-    steps (whole replays of the K-step graph, back to back, so the clocks are
-    at their steady state under load when timing starts);
-  * timed region: exactly K steps captured in one HIP graph (so host launch
-    overhead is not measured), replayed once between two synchronisations;
-    GPU time from events around the replay gives ms_per_step and ``value``.
-  * the roofline's ``achieved`` divides the ideal bytes by the average launch
-    duration over the timed region (GPU time of the replay / K: one kernel per
-    step, so this includes the short gaps between back-to-back kernels).
-  * ``kernel_us`` (extra): the same K calls launched eagerly, each between two
-    events on the launch stream, behind a spin kernel that lets the host queue
-    them all first.
+Order of work on the GPU:
+  * one call on input set 0, its output copied to the host (checked against
+    the oracle after the timing, on the CPU);
+  * the streaming-read references (libnvfp4bench.so, four read designs) on
+    buffers of the same byte count, each timed like the GEMV; the best one is
+    reported as ``attainable``;
+  * the GEMV: exactly W untimed warmup steps, then a short spin on the GPU
+    while the host enqueues a start event, K steps and an end event behind
+    it, so the GPU runs the K steps back to back; between two
+    synchronisations. ``ms_per_step`` = GPU time between the events / K, and
+    ``value`` = ideal bytes / that. The roofline's ``achieved`` is the same
+    quotient: one kernel per step, so the average launch duration over the
+    timed region (back-to-back launches, gaps included).
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -45,7 +45,7 @@ METRIC = "Âµs/call and achieved HBM GB/s (% of peak) for NVFP4 GEMV 7168Ã—16384Ã
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 512 * 2 ** 20
 WORKLOADS = {"headline": synth.HEADLINE, "balanced": synth.BALANCED, "batched": synth.BATCHED,
-             "tiny": synth.TINY}
+             "tiny": synth.TINY, "shard": synth.SHARD}
 for _w in synth.EDGE:
     WORKLOADS[_w.name] = _w
 
@@ -77,62 +77,109 @@ def traffic_from_profile(workload_name: str, layout: str):
     return d.get("hbm_bytes_per_launch")
 
 
+BOX_CPU_SHARE = 16   # host threads a one-GPU machine allots to a job
+SUBMIT_SPIN_CYCLES = 4_000_000   # GPU clock cycles (about 2 ms) of spin ahead of the timed steps
+SPIN_CYCLES_PER_STEP = 60_000    # and at least this much per timed step (host enqueue time)
+
+
 def cpu_baseline(w, layout: str, budget_s: float):
-    """The oracle as it stands, on this host's cores, on input set 0."""
+    """The oracle as it stands (never tuned for this) on input set 0: the
+    median of 3 timed runs on the one-GPU machine's CPU share (16 threads, fewer if
+    the host has fewer), and the median of 3 on one thread, each over a row
+    sample (rows repeat past M*L) scaled to one full call; about ``budget_s``
+    seconds of CPU work in all."""
+    import statistics
     import oracle
     oracle.build(force=False)
-    cores = min(os.cpu_count() or 1, 16)
+    host = os.cpu_count() or 1
+    nth = min(host, BOX_CPU_SHARE)
     inp = synth.make_inputs(w, 0)
-    # bounded sample: whole calls if one fits the budget, else a row subset
-    t0 = time.perf_counter()
-    oracle.gemv_rows(inp, np.arange(min(256, w.M * w.L)), layout, nthreads=cores)
-    per_row = (time.perf_counter() - t0) / min(256, w.M * w.L)
     rows_total = w.M * w.L
-    if per_row * rows_total <= budget_s / 2:
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.gemv(inp, layout, nthreads=cores)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 50:
-                break
-        sec_per_call = el / reps
-        sample = f"{reps} full {w.name} calls on input set 0 ({layout} scales)"
-    else:
-        nrows = max(1, int(budget_s / per_row))
-        rows = np.arange(nrows) % rows_total
+
+    def sec_per_row(nthreads: int, nrows: int) -> float:
+        rows = np.arange(nrows, dtype=np.int64) % rows_total
         t0 = time.perf_counter()
-        oracle.gemv_rows(inp, rows, layout, nthreads=cores)
-        el = time.perf_counter() - t0
-        sec_per_call = el / nrows * rows_total
-        sample = f"{nrows} of {rows_total} rows of {w.name} input set 0, scaled to a full call"
-    return {"value": round(w.ideal_bytes / sec_per_call / 1e9, 4), "unit": "GB/s",
-            "cores": cores, "kind": "oracle", "sample": sample,
-            "us_per_call": round(sec_per_call * 1e6, 1)}
+        oracle.gemv_rows(inp, rows, layout, nthreads=nthreads)
+        return (time.perf_counter() - t0) / nrows
+
+    share = budget_s / 6.0                               # 3 runs on each setting
+    out = {}
+    for label, threads in (("multi", nth), ("one", 1)):
+        probe = sec_per_row(threads, max(64, 8 * threads))
+        nrows = int(max(8 * threads, min(50 * rows_total, share / probe)))
+        times = [sec_per_row(threads, nrows) * rows_total for _ in range(3)]
+        out[label] = (statistics.median(times), nrows)
+    sec, nrows = out["multi"]
+    sec1, nrows1 = out["one"]
+    return {"value": round(w.ideal_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": (f"median of 3 runs of {nrows} rows ({nth} threads) and of 3 runs of {nrows1} rows "
+                       f"(1 thread) of {w.name} input set 0, {layout} scales, each scaled to a full call of "
+                       f"{rows_total} rows"),
+            "us_per_call": round(sec * 1e6, 1), "host_cpus": host,
+            "one_thread": {"value": round(w.ideal_bytes / sec1 / 1e9, 4), "unit": "GB/s",
+                           "us_per_call": round(sec1 * 1e6, 1)}}
 
 
-def timed_graph(step, steps: int, warmup: int):
-    """Capture ``steps`` calls of ``step(i, stream)`` in one HIP graph, replay it
-    back to back until at least ``warmup`` untimed steps have run (the clocks
-    reach their steady state under load), then time exactly one replay between
-    two synchronisations. Returns (ms per step, warmup steps run)."""
+def timed_steps(step, steps: int, warmup: int):
+    """Launch exactly ``warmup`` untimed steps, then a spin on the GPU long
+    enough for the host to enqueue the start event, ``steps`` timed steps and
+    the end event behind it, so that the GPU runs the timed steps back to back
+    (no host launch latency inside the interval; a HIP graph replay measured
+    the same per-step time for 200 steps and carried a fixed cost of its own
+    for 20). Returns (ms per step, warmup)."""
     import torch
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.graph(graph, stream=cap):
-        for i in range(steps):
-            step(i, cap)
+    st = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    reps = max(1, -(-warmup // steps))
-    for _ in range(reps):
-        graph.replay()
-    torch.cuda.synchronize()
+    for i in range(warmup):
+        step(i, st)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(max(SUBMIT_SPIN_CYCLES, SPIN_CYCLES_PER_STEP * steps))
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
-    graph.replay()
+    for i in range(steps):
+        step(i, st)
     ev1.record()
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps, reps * steps
+    return ev0.elapsed_time(ev1) / steps, warmup
+
+
+def attainable_read(nbytes: int, steps: int, warmup: int, dev):
+    """The streaming-read reference in each design on rotating random buffers
+    of about ``nbytes`` (rounded down to the design's unit), timed like the
+    GEMV. Returns (the design with the highest GB/s, {design: us per call})."""
+    import torch
+    from block_scaled_fp4_gemv_amd import benchlib
+    per_mode = {}
+    best = None
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12345)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    for mode in sorted(benchlib.STREAM_READ_MODES):
+        unit = benchlib.stream_read_unit(mode)
+        rd_bytes = nbytes // unit * unit
+        if rd_bytes == 0:
+            continue
+        rd_sets = max(1, min(64, -(-ROTATE_BYTES // rd_bytes)))
+        # random bytes, like the GEMV's operands (HBM power, and so clocks, depend on the data)
+        bufs = [torch.randint(0, 256, (rd_bytes,), dtype=torch.uint8, device=dev, generator=gen)
+                for _ in range(rd_sets)]
+
+        def rd_step(i, stream=None, mode=mode, bufs=bufs, rd_bytes=rd_bytes, rd_sets=rd_sets):
+            benchlib.stream_read(bufs[i % rd_sets], rd_bytes, sink, mode, stream)
+        ms, _ = timed_steps(rd_step, steps, warmup)
+        gbs = rd_bytes / (ms * 1e-3) / 1e9
+        per_mode[str(mode)] = {"bytes": rd_bytes, "us_per_call": round(ms * 1e3, 3), "GB/s": round(gbs, 2)}
+        log(f"attainable: read design {mode}, {rd_bytes} B: {ms * 1e3:.3f} us per call, {gbs:.0f} GB/s")
+        if best is None or gbs > best[1]:
+            best = (mode, gbs, rd_bytes, ms)
+        del bufs
+    if best is None:
+        return None, per_mode
+    mode, gbs, rd_bytes, ms = best
+    return ({"kind": "streaming read of the same byte count (libnvfp4bench.so)",
+             "design": benchlib.STREAM_READ_MODES[mode], "bytes": rd_bytes, "us_per_call": round(ms * 1e3, 3),
+             "GB/s": round(gbs, 2), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+             "by_design": per_mode}, per_mode)
 
 
 def bench_small_n(args, w, dev):
@@ -175,7 +222,7 @@ def bench_small_n(args, w, dev):
                                   nthreads=min(os.cpu_count() or 1, 16))
         verified = bool(oracle.check(got, ref).all())
         log(f"small-N parity vs oracle on set 0: {'ok' if verified else 'FAILED'}")
-    ms, warm = timed_graph(step, args.steps, args.warmup)
+    ms, warm = timed_steps(step, args.steps, args.warmup)
     gbs = ideal / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": f"Âµs/call and achieved HBM GB/s of the {N}-vector NVFP4 skinny GEMM",
@@ -214,7 +261,7 @@ def bench_reblock(args, w, dev):
         log(f"reblock parity vs oracle: {'ok' if verified else 'FAILED'}")
     def rstep(i, stream=None):
         g.nvfp4_scales_to_blocked(plains[i % nsets], outs[i % nsets], M, K, L, stream)
-    ms, warm = timed_graph(rstep, args.steps, args.warmup)
+    ms, warm = timed_steps(rstep, args.steps, args.warmup)
     gbs = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
     out = {"metric": "Âµs/call and achieved HBM GB/s of the plain -> 128x4 blocked SFA reblock",
            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -247,12 +294,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed steps before the timed region (whole replays of the K-step graph)")
+                    help="untimed steps right before the timed steps")
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
     ap.add_argument("--layout", default="blocked", choices=["blocked", "plain"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-attainable", action="store_true", help="skip the streaming-read references")
     ap.add_argument("--small-n", type=int, default=0, metavar="N",
                     help="time the N-vector skinny GEMM (N = 1..8) on the workload's A instead "
                          "(its own JSON line)")
@@ -320,67 +368,34 @@ def main():
         s = sets[i % nsets]
         g.nvfp4_gemv(s["a"], s["b"], s["sfa"], s["sfb"], s["c"], M, K, L, layout, stream)
 
-    # ---- one call first (allocates any split-K workspace before graph capture)
+    # ---- one call first (allocates any split-K workspace before timing
+    # capture); its output is checked against the oracle after the timing
     step(0)
     torch.cuda.synchronize()
+    got0 = sets[0]["c"].cpu().view(torch.int16).numpy().view(np.uint16).reshape(L, M).copy()
+    K_steps = args.steps
 
-    # ---- correctness of the benchmarked configuration (set 0) against the
-    # oracle, before the warmup so the GPU is not left idle before timing
+    # ---- attainable: streaming reads of the same byte count, each design
+    # timed like the GEMV
+    attainable = None
+    if not args.no_attainable:
+        attainable, _ = attainable_read(w.ideal_bytes, K_steps, args.warmup, dev)
+
+    # ---- the timed region: exactly W warmup steps, then K back-to-back steps
+    t0 = time.perf_counter()
+    ms_per_step, warm = timed_steps(step, K_steps, args.warmup)
+    wall_s = time.perf_counter() - t0
+    log(f"timed: {K_steps} steps after {warm} warmup steps, {ms_per_step * K_steps:.3f} ms GPU "
+        f"({wall_s * 1e3:.1f} ms wall incl. warmup)")
+
+    # ---- correctness of the benchmarked configuration (set 0) against the oracle
     verified = None
     if not args.no_verify:
         import oracle
         oracle.build(force=False)
-        got = sets[0]["c"].cpu().view(torch.int16).numpy().view(np.uint16).reshape(L, M)
-        ref = oracle.gemv(inp0, layout, nthreads=min(os.cpu_count() or 1, 16))
-        verified = bool(oracle.check(got, ref).all())
+        ref = oracle.gemv(inp0, layout, nthreads=min(os.cpu_count() or 1, BOX_CPU_SHARE))
+        verified = bool(oracle.check(got0, ref).all())
         log(f"parity vs oracle on set 0: {'ok' if verified else 'FAILED'}")
-
-    # ---- warmup, then the timed region: exactly K steps in one graph replay
-    K_steps = args.steps
-    t0 = time.perf_counter()
-    ms_per_step, warm = timed_graph(step, K_steps, args.warmup)
-    wall_s = time.perf_counter() - t0
-    log(f"timed: {K_steps} steps after {warm} warmup steps, {ms_per_step * K_steps:.3f} ms GPU "
-        f"({wall_s * 1e3:.1f} ms wall incl. capture and warmup)")
-
-    # ---- attainable: a plain streaming read of the same byte count (rounded
-    # down to 256 KiB), same pattern, same launch and timing method
-    rd_bytes = w.ideal_bytes // (256 * 1024) * (256 * 1024)
-    attainable = None
-    if rd_bytes > 0:
-        rd_sets = max(1, min(64, -(-ROTATE_BYTES // rd_bytes)))
-        # random bytes, like the GEMV's operands (HBM power, and so clocks, depend on the data)
-        rd_gen = torch.Generator(device=dev)
-        rd_gen.manual_seed(12345)
-        rd_bufs = [torch.randint(0, 256, (rd_bytes,), dtype=torch.uint8, device=dev, generator=rd_gen)
-                   for _ in range(rd_sets)]
-        sink = torch.zeros(256, dtype=torch.int32, device=dev)
-
-        def rd_step(i, stream=None):
-            g.nvfp4_stream_read(rd_bufs[i % rd_sets], rd_bytes, sink, stream)
-        rd_ms, _ = timed_graph(rd_step, K_steps, args.warmup)
-        rd_gbs = rd_bytes / (rd_ms * 1e-3) / 1e9
-        attainable = {"kind": "nvfp4_stream_read: one streaming read of the same byte count",
-                      "bytes": rd_bytes, "us_per_call": round(rd_ms * 1e3, 3), "GB/s": round(rd_gbs, 2),
-                      "pct_of_peak": round(100 * rd_gbs / PEAK_HBM_GBS, 2)}
-        log(f"attainable: streaming read of {rd_bytes} B: {rd_ms * 1e3:.3f} us per call, {rd_gbs:.0f} GB/s")
-        del rd_bufs
-
-    # ---- per-kernel durations: eager launches bracketed by events
-    st = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(2e8))       # let the host queue every launch first
-    for i in range(K_steps):
-        starts[i].record(st)
-        step(i, st)
-        ends[i].record(st)
-    torch.cuda.synchronize()
-    durs_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
-    kern_avg, kern_med = float(durs_us.mean()), float(np.median(durs_us))
-    log(f"kernel: avg {kern_avg:.2f} us, median {kern_med:.2f} us, min {durs_us.min():.2f}, "
-        f"p90 {np.percentile(durs_us, 90):.2f}")
 
     ideal = w.ideal_bytes
     value_gbs = ideal / (ms_per_step * 1e-3) / 1e9
@@ -403,9 +418,6 @@ def main():
                    "rotating_sets": nsets, "ideal_bytes_per_call": ideal, "plan": plan},
         "us_per_call": round(ms_per_step * 1e3, 3),
         "pct_of_peak": round(100 * value_gbs / PEAK_HBM_GBS, 2),
-        "kernel_us": {"avg": round(kern_avg, 3), "median": round(kern_med, 3),
-                      "min": round(float(durs_us.min()), 3),
-                      "p90": round(float(np.percentile(durs_us, 90)), 3)},
         "verified_vs_oracle": verified,
         "attainable": attainable,
         # GB/s of the GEMV over GB/s of the streaming read

@@ -50,7 +50,6 @@ EXPORTED_SYMBOLS = (
     "nvfp4_gemm_small_n_plan",
     "nvfp4_scales_to_blocked",
     "nvfp4_blocked_scales_bytes",
-    "nvfp4_stream_read",
     "nvfp4_status_string",
     "nvfp4_last_hip_error",
 )
@@ -132,8 +131,6 @@ def lib():
     L.nvfp4_scales_to_blocked.argtypes = [vp, vp, i64, i64, i64, vp]
     L.nvfp4_blocked_scales_bytes.restype = ctypes.c_size_t
     L.nvfp4_blocked_scales_bytes.argtypes = [i64, i64, i64]
-    L.nvfp4_stream_read.restype = i32
-    L.nvfp4_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_last_hip_error.restype = i32
@@ -353,20 +350,6 @@ def nvfp4_scales_to_blocked(plain, blocked, rows: int, K: int, L: int, stream=No
     st = lib().nvfp4_scales_to_blocked(pp, pb, rows, K, L, _stream_handle(stream))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_scales_to_blocked")
-
-
-def nvfp4_stream_read(src, nbytes: int, sink, stream=None) -> None:
-    """Enqueue the streaming-read reference over the first ``nbytes`` bytes of
-    ``src`` (a measurement helper, not part of the GEMV); ``sink`` holds at
-    least 256 uint32."""
-    (ps, ns), (pk, nk) = _ptr_and_bytes(src), _ptr_and_bytes(sink)
-    if ns is not None and ns < nbytes:
-        raise ValueError(f"src holds {ns} bytes, asked to read {nbytes}")
-    if nk is not None and nk < 1024:
-        raise ValueError(f"sink holds {nk} bytes, needs 1024")
-    st = lib().nvfp4_stream_read(ps, nbytes, pk, _stream_handle(stream))
-    if st != NVFP4_OK:
-        raise Nvfp4Error(st, "nvfp4_stream_read")
 
 
 def nvfp4_status_string(status: int) -> str:

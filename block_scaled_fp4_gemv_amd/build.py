@@ -13,10 +13,13 @@ from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("nvfp4_gemv.hip", "nvfp4_reblock.hip", "nvfp4_gemm_small_n.hip",
-                                                    "nvfp4_stream_read.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("nvfp4_gemv.hip", "nvfp4_reblock.hip", "nvfp4_gemm_small_n.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4gemv.so")
+# the measurement helper (streaming-read reference for the bench): its own library
+BENCH_SRCS = [os.path.join(PKG, "csrc", "bench", "stream_read.hip")]
+BENCH_INCLUDE = os.path.join(PKG, "csrc", "bench")
+BENCH_LIB = os.path.join(PKG, "libnvfp4bench.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -41,14 +44,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def build(extra_flags=None, out: str = LIB, verbose: bool = False) -> str:
-    """Compile the HIP sources in csrc/ into ``out`` (one object per source,
-    compiled in parallel, then linked). Always recompiles."""
+def _build_lib(srcs, include, out, extra_flags, verbose):
     tmp = out + ".tmp"
     with tempfile.TemporaryDirectory(prefix="nvfp4_build_") as td:
-        objs = [os.path.join(td, os.path.basename(src) + ".o") for src in SRCS]
-        cmds = [[hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-c", src, "-o", obj]
-                for src, obj in zip(SRCS, objs)]
+        objs = [os.path.join(td, os.path.basename(src) + ".o") for src in srcs]
+        cmds = [[hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", include, "-c", src, "-o", obj]
+                for src, obj in zip(srcs, objs)]
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
@@ -62,6 +63,18 @@ def build(extra_flags=None, out: str = LIB, verbose: bool = False) -> str:
             print(" ".join(link), flush=True)
         subprocess.run(link, check=True)
     os.replace(tmp, out)
+    return out
+
+
+def build(extra_flags=None, out: str = LIB, verbose: bool = False) -> str:
+    """Compile the HIP sources in csrc/ into ``out`` (one object per source,
+    compiled in parallel, then linked), and the measurement helper into
+    libnvfp4bench.so. Always recompiles."""
+    with ThreadPoolExecutor(max_workers=2) as ex:
+        f1 = ex.submit(_build_lib, SRCS, INCLUDE, out, extra_flags, verbose)
+        f2 = ex.submit(_build_lib, BENCH_SRCS, BENCH_INCLUDE, BENCH_LIB, extra_flags, verbose)
+        f1.result()
+        f2.result()
     return out
 
 

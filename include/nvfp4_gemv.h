@@ -273,24 +273,6 @@ nvfp4_status_t nvfp4_scales_to_blocked(const void *plain, void *blocked, int64_t
 /* Bytes of the blocked layout for (rows, K, L); 0 for an invalid shape. */
 size_t nvfp4_blocked_scales_bytes(int64_t rows, int64_t K, int64_t L);
 
-/*
- * Streaming-read reference, for measurement only (it is not a step of the
- * method): reads `bytes` bytes at `src` once, with the access pattern of the
- * GEMV's A stream (256 workgroups, each a contiguous slice read in 1 KiB
- * pieces, 8 non-temporal 16-byte loads in flight per lane) and computes
- * nothing. Its time per call is what a plain read of that many bytes attains
- * on this machine, launch and ramp included: the bench reports the GEMV
- * against it ("% of attainable") beside the % of the HBM peak.
- *
- *   src   DEVICE pointer, 16-byte aligned, `bytes` readable bytes
- *   bytes a multiple of 256 KiB, at most 256 * (2^31 - 1)
- *   sink  DEVICE pointer to 256 uint32 (4-byte aligned); written only in the
- *         unlikely case that a lane's XOR of its data equals a fixed constant
- * Errors (null pointer, bad size, misalignment) are reported before any HIP
- * call; the call only enqueues work on `stream`.
- */
-nvfp4_status_t nvfp4_stream_read(const void *src, size_t bytes, void *sink, void *stream);
-
 /* Static description of a status code (never NULL). */
 const char *nvfp4_status_string(int status);
 

@@ -81,7 +81,9 @@ BALANCED = Workload("balanced_7168x2048x4", 7168, 2048, 4, "uniform", 1)
 BATCHED = Workload("batched_4096x7168x8", 4096, 7168, 8, "uniform", 2)
 HEADLINE = Workload("headline_7168x16384x1", 7168, 16384, 1, "uniform", 3)
 EDGE = _edge_workloads()
-ALL = [TINY, BALANCED, BATCHED, HEADLINE] + EDGE
+# one GPU's share of the headline split 8 ways along M (whole 128-row blocks)
+SHARD = Workload("shard_896x16384x1", 896, 16384, 1, "uniform", 5)
+ALL = [TINY, BALANCED, BATCHED, HEADLINE] + EDGE + [SHARD]
 
 
 def rng_for(w: Workload, set_idx: int = 0, seed: int = 0) -> np.random.Generator:

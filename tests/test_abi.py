@@ -283,17 +283,6 @@ def test_small_n_plan():
         g.nvfp4_gemm_small_n_plan(128, 9, 256, 1)
 
 
-def test_stream_read_validation():
-    L = g.lib()
-    unit = 256 * 1024
-    assert L.nvfp4_stream_read(None, unit, A16, None) == g.NVFP4_ERR_NULL_POINTER
-    assert L.nvfp4_stream_read(A16, unit, None, None) == g.NVFP4_ERR_NULL_POINTER
-    for bad in (0, unit - 16, unit + 1024):
-        assert L.nvfp4_stream_read(A16, bad, A16, None) == g.NVFP4_ERR_INVALID_SHAPE, bad
-    assert L.nvfp4_stream_read(A16 + 8, unit, A16, None) == g.NVFP4_ERR_MISALIGNED
-    assert L.nvfp4_stream_read(A16, unit, A16 + 2, None) == g.NVFP4_ERR_MISALIGNED
-
-
 def test_noalloc_validation_before_launch():
     lib = g.lib()
     args = [OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"], OK_ARGS["c"], 128, 256, 1, 0, None]

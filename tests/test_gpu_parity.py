@@ -130,7 +130,7 @@ def test_hand_cases_bit_exact(case, layout):
 
 # ---------------------------------------------------------------- workloads
 
-MAIN = [synth.TINY, synth.BALANCED, synth.BATCHED, synth.HEADLINE]
+MAIN = [synth.TINY, synth.BALANCED, synth.BATCHED, synth.HEADLINE, synth.SHARD]
 
 
 @pytest.mark.parametrize("w", MAIN, ids=lambda w: w.name)

@@ -72,12 +72,16 @@ constexpr int kCpl = 4;                   // chunks per lane per K-segment
 constexpr int kPrefetch = 8;              // chunk loads in flight per lane (multiple of kCpl)
 constexpr int kDeferRounds = 2;           // first row rounds that keep block sums (multiple of the ring's rounds)
 constexpr int kMaxLpr = 256;              // lanes per row, at most the compute threads
-constexpr int kSfaLdsBudget = 36 * 1024;  // staged SFA bytes per workgroup (B, SFB and sums fit in 64 KiB)
+constexpr int kLdsLimit = 159 * 1024;     // dynamic LDS of one workgroup (gfx950: 160 KiB per CU)
+constexpr int kSfaLdsBudget = 36 * 1024;  // staged SFA bytes per workgroup
+constexpr int kStageInFlight = 48;        // staging copies in flight at most (the counter holds 63)
 constexpr int kDmaBytes = 64 * 16;        // LDS bytes one wave-wide 16-byte direct-to-LDS load fills
 constexpr bool kStageB = true;            // blocked layout: B is staged with SFB (else the computing waves load it)
 constexpr int kSfaAhead = 20;             // blocked: A-scale copies issued before the wait for b's inputs
 constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
 constexpr int kBFirstMaxRounds = 8;       // b's inputs go first for workgroups of at most this many row rounds
+constexpr int64_t kWgStartSlots = 7;      // start-up of one workgroup, in slots of streaming (measured: about
+                                          // 1.7 us against 0.24 us per slot of 4 rows x 2 KiB)
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
 constexpr int kCachePolicyNT = 2;         // buffer load cache policy: non-temporal
@@ -334,8 +338,14 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                 const int32_t nload = (per * nmajor + 63) >> 6;
                 const int32_t dmaj = 64 / per, dmin = 64 % per;
                 int32_t mn = lane % per, mj = lane / per;
-                auto issue = [&](int32_t i0, int32_t i1) {
+                // PACED: at most kStageInFlight copies in flight (b's inputs
+                // count: they were issued first); only compiled in where the
+                // copies could outnumber what the wait counter holds
+                auto issue_loop = [&](auto paced, int32_t i0, int32_t i1) {
                     for (int32_t i = i0; i < i1; ++i) {
+                        if (decltype(paced)::value && i + nbc * NV + nsfb * NV >= kStageInFlight)
+                            __builtin_amdgcn_s_waitcnt((kWaitVmcnt0 & ~0xC00F) | ((kStageInFlight - 1) & 15) |
+                                                       (((kStageInFlight - 1) >> 4) << 14));
                         const int32_t mjc = min(mj, nmajor - 1);
                         const uint8_t *src;
                         if (LAYOUT == NVFP4_SF_BLOCKED) {
@@ -353,6 +363,13 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
                             ++mj;
                         }
                     }
+                };
+                const bool many = NV * (nbc + nsfb) + nload > kStageInFlight;
+                auto issue = [&](int32_t i0, int32_t i1) {
+                    if (many)
+                        issue_loop(std::true_type{}, i0, i1);
+                    else
+                        issue_loop(std::false_type{}, i0, i1);
                 };
                 if (STAGE_SFB) {
                     // A CU holds only so many loads in flight; issuing every
@@ -779,10 +796,27 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
 
     // Slots per workgroup: tiles never straddle a batch, so a batch has
     // P = ceil(ns / spw) workgroups. Among grids of at most k * kTargetWGs
-    // workgroups (k = 1, 2, ...), take the one whose busiest CU holds the
-    // fewest slots (ceil(grid / 256) workgroups of spw slots), then the
-    // smaller grid: e.g. 258 workgroups would leave two CUs with twice the work.
-    const int64_t spw_max = std::max<int64_t>(1, kSfaLdsBudget / (32 * pl.lpr));
+    // workgroups (k = 1, 2, ...), take the one whose busiest CU costs least,
+    // then the smaller grid: its ceil(grid / 256) workgroups of spw slots
+    // each cost a start-up of kWgStartSlots slots (b', the staged scales and
+    // the first round of loads all wait on memory latency; workgroups that
+    // share a CU do not overlap it) plus their slots. E.g. 258 workgroups
+    // would leave two CUs with twice the work, and three 1-slot workgroups per
+    // CU cost more than one 4-slot workgroup.
+    // a workgroup's LDS: staged SFA, staged B, staged blocked SFB, per-wave row sums
+    const int wpg = pl.lpr > 64 ? pl.lpr / 64 : 1;
+    auto lds_of = [&](int64_t spw_) {
+        return (int64_t)stage_bytes(pl.lpr, spw_) + nv * (kStageB ? align_up((size_t)(64 * pl.lpr), kDmaBytes) : 0) +
+               nv * align_up((size_t)(32 * pl.lpr), kDmaBytes) + 4 * spw_ * wpg * nv * (int64_t)sizeof(float);
+    };
+    // The scales of a workgroup's rows are staged before its rounds can be
+    // finished, so large stages delay every workgroup's start: keep them to
+    // kSfaLdsBudget (measured: 88-row workgroups staging 88 KiB ran 37.8 us on
+    // 7168x16384x3 against 35.5 us for three 28-row workgroups per CU).
+    int64_t spw_max = 1;
+    while (spw_max < pl.ns && lds_of(spw_max + 1) <= kLdsLimit &&
+           stage_bytes(pl.lpr, spw_max + 1) <= kSfaLdsBudget)
+        ++spw_max;
     int64_t spw = 1;
     if (total_slots >= kTargetWGs) {
         int64_t best_cost = INT64_MAX, best_grid = INT64_MAX;
@@ -792,7 +826,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
             if (cand > spw_max)
                 continue;
             const int64_t grid = L * S * cdiv(pl.ns, cand);
-            const int64_t cost = cdiv(grid, kTargetWGs) * cand;
+            const int64_t cost = cdiv(grid, kTargetWGs) * (kWgStartSlots + cand);
             if (cost < best_cost || (cost == best_cost && grid < best_grid)) {
                 best_cost = cost;
                 best_grid = grid;
@@ -805,12 +839,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
     pl.spw = (int)spw;
     pl.P = (int)cdiv(pl.ns, spw);
     pl.n_wg = (int64_t)pl.P * L * S;
-    const int wpg = pl.lpr > 64 ? pl.lpr / 64 : 1;
     pl.stage_bytes = stage_bytes(pl.lpr, spw);
-    // staged SFA, staged B, staged blocked SFB, per-wave row sums
-    pl.lds_bytes = (int)(pl.stage_bytes + nv * (kStageB ? align_up((size_t)(64 * pl.lpr), kDmaBytes) : 0) +
-                         nv * align_up((size_t)(32 * pl.lpr), kDmaBytes) +
-                         4 * spw * wpg * nv * (int)sizeof(float));
+    pl.lds_bytes = (int)lds_of(spw);
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
     // row rounds of a full workgroup: 4*spw rows, kThreads/lpr rows per round
     pl.bfirst = cdiv(4 * spw * pl.lpr, kThreads) <= kBFirstMaxRounds ? 1 : 0;

@@ -135,7 +135,7 @@ def test_plans(w):
     ns = 32 * (w.M // 128) + min(32, w.M % 128)
     tiles = synth.ceil_div(ns, p["rows_per_wg"] // 4)
     assert p["workgroups"] == tiles * w.L * p["k_splits"]
-    assert p["lds_bytes"] <= 64 * 1024
+    assert p["lds_bytes"] <= 159 * 1024       # a workgroup fits the CU's 160 KiB of LDS
     assert p["threads_per_wg"] == 320          # 4 computing waves and the staging wave
 
 

@@ -80,6 +80,8 @@ constexpr bool kStageB = true;            // blocked layout: B is staged with SF
 constexpr int kSfaAhead = 20;             // blocked: A-scale copies issued before the wait for b's inputs
 constexpr int64_t kTargetWGs = 256;       // one workgroup per CU
 constexpr int kBFirstMaxRounds = 8;       // b's inputs go first for workgroups of at most this many row rounds
+constexpr int64_t kSplitCostBytes = 50 * 1024; // a K-split's partials, ticket and ordered sum, in bytes of
+                                          // one workgroup's streaming (about 1.8 us at a CU's share)
 constexpr int64_t kWgStartSlots = 7;      // start-up of one workgroup, in slots of streaming (measured: about
                                           // 1.7 us against 0.24 us per slot of 4 rows x 2 KiB)
 constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
@@ -784,9 +786,22 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
 
     int64_t S = 1;
     if (total_slots < kTargetWGs) {
-        // too few rows to fill the machine: split K, keeping >= 256 chunks per
-        // slice so that one slot (4 rows) still occupies every lane
-        S = std::max<int64_t>(1, std::min<int64_t>(kTargetWGs / total_slots, nchunks / 256));
+        // Too few rows to fill the machine: K may be split, keeping >= 256
+        // chunks per slice so that one slot (4 rows) still occupies every
+        // lane. A split saves streaming time per workgroup but costs the
+        // float32 partials, the ticket and the ordered sum (about 1.8 us,
+        // measured): take the S with the least bytes per workgroup (one slot:
+        // 4 rows of A and their scales) plus kSplitCostBytes when S > 1.
+        const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(kTargetWGs / total_slots, nchunks / 256));
+        int64_t best = INT64_MAX;
+        for (int64_t cand = 1; cand <= s_max; ++cand) {
+            const int64_t slice = cdiv(nchunks, cand) * 16;            // bytes of A per row and slice
+            const int64_t cost = 4 * (slice + slice / 8) + (cand > 1 ? kSplitCostBytes : 0);
+            if (cost < best) {
+                best = cost;
+                S = cand;
+            }
+        }
     }
     const int64_t kc = cdiv(nchunks, S);
     S = cdiv(nchunks, kc);

@@ -78,7 +78,7 @@ def test_bad_layout(layout):
 
 def test_ex_workspace_errors():
     lib = g.lib()
-    M, K, L = 127, 16384, 1
+    M, K, L = 16, 32768, 1                      # a shape the plan splits along K
     need = lib.nvfp4_gemv_workspace_bytes(M, K, L)
     assert need > 0
     base = (OK_ARGS["a"], OK_ARGS["b"], OK_ARGS["sfa"], OK_ARGS["sfb"], OK_ARGS["c"], M, K, L, 1)
@@ -109,7 +109,7 @@ def test_scaled_validation_order():
 
 
 def test_scaled_workspace_errors():
-    M, K, L = 127, 16384, 1
+    M, K, L = 16, 32768, 1                      # a shape the plan splits along K
     need = g.lib().nvfp4_gemv_workspace_bytes(M, K, L)
     assert need > 0
     assert scaled(0.5, None, need, M, K, L) == g.NVFP4_ERR_WORKSPACE       # NULL with a size
@@ -122,7 +122,8 @@ def test_workspace_bytes():
     for w in (synth.BALANCED, synth.BATCHED, synth.HEADLINE, synth.TINY):
         assert lib.nvfp4_gemv_workspace_bytes(w.M, w.K, w.L) == 0, w.name
     assert lib.nvfp4_gemv_workspace_bytes(0, 256, 1) == 0
-    assert lib.nvfp4_gemv_workspace_bytes(127, 16384, 1) % 256 == 0
+    assert lib.nvfp4_gemv_workspace_bytes(16, 32768, 1) % 256 == 0
+    assert lib.nvfp4_gemv_workspace_bytes(127, 16384, 3) == 0    # a split would cost more than it saves
 
 
 @pytest.mark.parametrize("w", synth.ALL, ids=lambda w: w.name)
@@ -146,7 +147,7 @@ def test_long_k_is_segmented_not_split():
 
 
 def test_split_only_for_small_grids():
-    for M, K, L in [(127, 16384, 1), (1000, 4096, 3), (1, 32768, 1), (5, 65536, 2)]:
+    for M, K, L in [(127, 16384, 1), (1000, 4096, 3), (1, 32768, 1), (5, 65536, 2), (127, 65536, 3)]:
         p = g.nvfp4_gemv_plan(M, K, L)
         ns = 32 * (M // 128) + min(32, M % 128)
         if p["k_splits"] > 1:

@@ -106,7 +106,7 @@ def test_sticky_tie_rows(top, tail):
     parity_scaled(inp, "blocked", float(ma) * 2.0 ** -34)
 
 
-@pytest.mark.parametrize("M,K,L", [(127, 16384, 1), (5, 32768, 2)])
+@pytest.mark.parametrize("M,K,L", [(16, 32768, 1), (5, 32768, 2)])
 def test_scaled_with_own_workspace(M, K, L):
     inp = synth.random_inputs(M, K, L, seed=26)
     dev = DeviceInputs(inp)

@@ -187,7 +187,7 @@ def test_sign_flip_negates_bit_exact(w):
     np.testing.assert_array_equal(y, -x)
 
 
-@pytest.mark.parametrize("M,K,L", [(7168, 16384, 1), (127, 16384, 3), (1000, 4096, 1)])
+@pytest.mark.parametrize("M,K,L", [(7168, 16384, 1), (127, 65536, 3), (1000, 4096, 1)])
 def test_deterministic(M, K, L):
     inp = synth.random_inputs(M, K, L, seed=3)
     dev = DeviceInputs(inp)
@@ -214,7 +214,7 @@ def test_batch_slices_match_single_batch_calls():
 
 # ---------------------------------------------------------------- entry points and streams
 
-@pytest.mark.parametrize("M,K,L", [(127, 16384, 1), (1000, 16384, 3), (7168, 2048, 4), (5, 32768, 2)])
+@pytest.mark.parametrize("M,K,L", [(16, 32768, 1), (127, 65536, 3), (1000, 16384, 3), (7168, 2048, 4), (5, 32768, 2)])
 def test_ex_with_own_workspace_matches_default(M, K, L):
     inp = synth.random_inputs(M, K, L, seed=11)
     dev = DeviceInputs(inp)

@@ -259,7 +259,8 @@ SHAPES = sorted({(w.M, w.K, w.L) for w in synth.ALL} |
                  (127, 16384, 3), (1000, 16384, 3), (7168, 2048, 4), (5, 32768, 2),
                  (33, 8192, 1), (1000, 4096, 3), (1000, 4096, 1), (256, 2048, 2), (4, 128, 16),
                  (7168, 32768, 1), (64, 65536, 1), (300, 20480, 2), (16, 256, 256), (2, 16384, 16),
-                 (1, 352, 1), (1, 384, 1), (1, 320, 1), (128, 256, 1), (300, 4128, 1)})
+                 (1, 352, 1), (1, 384, 1), (1, 320, 1), (128, 256, 1), (300, 4128, 1),
+                 (127, 65536, 3), (121, 65536, 2), (16, 32768, 1), (1, 1 << 22, 1)})
 
 
 @pytest.mark.parametrize("M,K,L", SHAPES)

@@ -50,7 +50,7 @@ def _oracle_built():
 
 def test_scratch_covers_every_split_workspace_of_these_shapes():
     cap = g.nvfp4_gemv_noalloc_scratch_bytes()
-    for M, K, L in [(127, 16384, 3), (5, 32768, 2), (64, 65536, 1), (1, 1 << 22, 1), (121, 16384, 4)]:
+    for M, K, L in [(127, 65536, 3), (5, 32768, 2), (64, 65536, 1), (1, 1 << 22, 1), (121, 65536, 2)]:
         assert 0 < g.nvfp4_gemv_workspace_bytes(M, K, L) <= cap
 
 
@@ -58,7 +58,7 @@ def test_scratch_covers_every_split_workspace_of_these_shapes():
 def test_calls_in_a_row_shrinking(layout):
     # split-K shapes (they use the scratch array), the second one smaller, then
     # a larger one again and a shape without a K-split
-    check(127, 16384, 3, layout, seed=1)
+    check(127, 65536, 3, layout, seed=1)
     check(5, 32768, 2, layout, seed=2, dist="edge")
     check(64, 65536, 1, layout, seed=3)
     check(1000, 4096, 1, layout, seed=4)

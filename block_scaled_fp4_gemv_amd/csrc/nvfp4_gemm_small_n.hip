@@ -156,13 +156,15 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
     if (s_begin < s_end) {
         uint4_t abuf[kMfRing][kMfRT], bbuf[kMfRing];
         uint32_t sabuf[kMfRing][kMfRT], sbbuf[kMfRing];
-        // loads of step s into a ring slot; every step index is clamped into
-        // [s_begin, s_end), so the ring's refills past the end re-read the last step
+        // loads of step s (s_begin <= s < s_end) into a ring slot. A is read
+        // with the default cache policy: a step takes 64 of a row's 128-byte
+        // line and the next step the other 64, which then hits L2 (with
+        // non-temporal loads about 5% of the lines were fetched twice)
         auto load_step = [&](int32_t s, int slot) {
             const int64_t ao = (int64_t)s * 64, so = (int64_t)s * kSfStep;
 #pragma unroll
             for (int t = 0; t < kMfRT; ++t) {
-                abuf[slot][t] = __builtin_nontemporal_load((const uint4_t *)(a_ptr[t] + ao));
+                abuf[slot][t] = *(const uint4_t *)(a_ptr[t] + ao);
                 sabuf[slot][t] = *(const uint16_t *)(sa_ptr[t] + so);
             }
             bbuf[slot] = *(const uint4_t *)(b_ptr + ao);
@@ -170,14 +172,16 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
         };
 #pragma unroll
         for (int d = 0; d < kMfRing; ++d) {
-            load_step(min(s_begin + d, s_end - 1), d);                 // in slot order, as in the loop
+            if (s_begin + d < s_end)                                   // in slot order, as in the loop
+                load_step(s_begin + d, d);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // whole rings with unconditional refills (a branch per slot here made
-        // the compiler drain the loads at every back-edge), then the steps
-        // already in the ring, without refills
+        // whole rings whose refills all fall before s_end, unconditional (a
+        // branch per slot here made the compiler drain the loads at every
+        // back-edge); then the last ring, refilled only up to s_end; then the
+        // steps still in the ring. No load reads past the wave's last step.
         int32_t s0 = s_begin;
-        for (; s0 + kMfRing <= s_end; s0 += kMfRing) {
+        for (; s0 + 2 * kMfRing <= s_end; s0 += kMfRing) {
 #pragma unroll
             for (int d = 0; d < kMfRing; ++d) {
                 // consume the slot, then refill it: its registers are reused
@@ -185,10 +189,21 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
                 // the ring live and the compiler drained the loads every ring)
                 mma_step(abuf[d], sabuf[d], bbuf[d], n_live ? sbbuf[d] : 0u);
                 __builtin_amdgcn_sched_barrier(0);                     // keep the refill here, not
-                load_step(min(s0 + d + kMfRing, s_end - 1), d);       // sunk to the end of the ring
+                load_step(s0 + d + kMfRing, d);                        // sunk to the end of the ring
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+#pragma unroll
+        for (int d = 0; d < kMfRing; ++d) {
+            if (s0 + d < s_end) {
+                mma_step(abuf[d], sabuf[d], bbuf[d], n_live ? sbbuf[d] : 0u);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s0 + d + kMfRing < s_end)
+                    load_step(s0 + d + kMfRing, d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        s0 += kMfRing;
 #pragma unroll
         for (int d = 0; d < kMfRing; ++d)
             if (s0 + d < s_end)

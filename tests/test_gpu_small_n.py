@@ -27,8 +27,9 @@ def _oracle_built():
 
 
 def blocked_rows(plain):
-    """Plain scales [L][rows][K/16] -> blocked bytes [L][per batch] (synth's view chain)."""
-    return synth.to_blocked(plain, pad=0)
+    """Plain scales [L][rows][K/16] -> blocked bytes [L][per batch] (synth's view
+    chain), padding bytes E4M3 NaN: a product that read one would show it."""
+    return synth.to_blocked(plain)
 
 
 def run_small_n(a, b, sfa, sfb, M, N, K, L, layout, alpha=1.0):
@@ -47,8 +48,12 @@ CASES = [(1, 1, 32, 1), (7, 3, 96, 2), (128, 2, 2048, 1), (300, 4, 20480, 2), (1
          # N = 2 through the GEMV kernel (ragged M, several batches, segmented K),
          # and N = 2 where a K-split is needed (the skinny kernel)
          (1000, 2, 4096, 3), (300, 2, 20480, 2), (127, 2, 16384, 1),
-         # matrix-core kernel over many batches, ragged M and K
-         (300, 4, 1056, 120), (100, 8, 160, 300)]
+         # register matrix-core kernel (K % 256 != 0) over many batches, ragged M and K
+         (300, 4, 1056, 120), (100, 8, 160, 300), (33, 3, 96, 5),
+         # staged matrix-core kernel (K % 256 == 0): partial last panels, one-tile
+         # workgroups, slots whose rows pass M, many batches
+         (5, 3, 768, 2), (127, 5, 2304, 3), (300, 6, 4352, 1), (1, 8, 256, 1), (129, 7, 256, 2),
+         (1000, 4, 7168, 2), (128, 4, 1280, 5)]
 
 
 @pytest.mark.parametrize("M,N,K,L", CASES)
@@ -78,12 +83,14 @@ def test_small_n_alpha_and_edge_codes(N):
         assert oracle.check_report(got, ref) == ""
 
 
-def test_small_n_headline_shape():
-    M, N, K, L = 7168, 8, 16384, 1
+@pytest.mark.parametrize("M,N,K,L", [(7168, 8, 16384, 1), (7168, 4, 16384, 1), (4096, 4, 7168, 8)])
+def test_small_n_headline_shape(M, N, K, L):
+    """The bench's shapes (N = 4 and 8 on the headline A, the batched A): sampled
+    rows of the first and last vector against the oracle."""
     a, b, sfa, sfb = inputs(M, N, K, L, 5)
     got = run_small_n(a, b, sfa, sfb, M, N, K, L, "blocked")
     rows = np.arange(0, M, 97)
-    for n in (0, 7):
+    for n in (0, N - 1):
         ref = oracle.gemm_small_n(a[:, rows], b[:, n:n + 1], sfa[:, rows], sfb[:, n:n + 1], rows.size, 1, K, L)
         col = oracle.Result(ref.c[:, 0], ref.s_f64[:, 0], ref.s_abs[:, 0], ref.s_exact[:, 0], ref.nan[:, 0])
         assert oracle.check(got[:, n, rows], col).all()

@@ -10,7 +10,10 @@
 // cols) is written as zero bytes.
 //
 // Work split. A workgroup of 256 threads owns one batch, one 128-row block
-// and kTilesPerWg consecutive tiles of it. It reads the 128 rows x 4*kTilesPerWg
+// and kTilesPerWg consecutive tiles of it. Workgroup ids are remapped so that
+// each XCD takes a contiguous range: the two workgroups that read the halves
+// of a row's 128-byte lines then share one L2 and each line is fetched once
+// (with ids dealt round-robin over the XCDs, every line was fetched twice). It reads the 128 rows x 4*kTilesPerWg
 // plain bytes row by row (consecutive threads take consecutive 16-byte units,
 // or words, of a row, so the reads are contiguous 64-byte runs of each row;
 // 16-byte loads where the rows allow them: 1.45x faster than words),
@@ -69,8 +72,12 @@ __global__ __launch_bounds__(kRbThreads) void nvfp4_reblock_kernel(const uint8_t
 {
     __shared__ uint32_t tile_words[128 * kLdsPitch];
     const int32_t t = threadIdx.x;
-    const int32_t wg = blockIdx.x % p.wg_per_rb;
-    const int64_t rbl = blockIdx.x / p.wg_per_rb;          // batch * nrb + row block
+    // contiguous ids per XCD (hardware id i runs on XCD i % 8), so that the
+    // workgroups sharing a row's 128-byte lines share an L2
+    const uint32_t n = gridDim.x, x = blockIdx.x % 8, j = blockIdx.x / 8;
+    const uint32_t lid = x * (n / 8) + min(x, n % 8) + j;
+    const int32_t wg = lid % p.wg_per_rb;
+    const int64_t rbl = lid / p.wg_per_rb;                 // batch * nrb + row block
     const int32_t l = (int32_t)(rbl / p.nrb), rb = (int32_t)(rbl % p.nrb);
     const int32_t cb0 = wg * kTilesPerWg;
     const uint8_t *in = plain + (int64_t)l * p.in_batch;

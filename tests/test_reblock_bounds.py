@@ -2,8 +2,8 @@
 run over its whole grid before it runs on a GPU: every plain read and every
 blocked write is inside its buffer, every blocked byte is written exactly once,
 and the bytes written are the view chain's (padding 0). Keep in step with the
-kernel: 256 threads, 16 tiles per workgroup, 16 words per row in LDS, rows
-read in 16-byte units when the row length is a multiple of 16 (and the input
+kernel: 256 threads, 16 tiles per workgroup, 16 words per row in LDS, workgroup
+ids remapped to contiguous ranges per XCD, rows read in 16-byte units when the row length is a multiple of 16 (and the input
 16-byte aligned), else in words or bytes."""
 import numpy as np
 import pytest
@@ -25,8 +25,14 @@ def emulate(plain, rows, K, L, aligned=True):
     writes = np.zeros(L * out_batch, np.int64)
     flat = plain.reshape(-1)
     t = np.arange(THREADS)
-    for bid in range(L * nrb * wg_per_rb):
-        wg, rbl = bid % wg_per_rb, bid // wg_per_rb
+    nwg = L * nrb * wg_per_rb
+    seen = set()
+    for bid in range(nwg):
+        x, j = bid % 8, bid // 8                            # contiguous logical ids per XCD
+        lid = x * (nwg // 8) + min(x, nwg % 8) + j
+        assert 0 <= lid < nwg and lid not in seen
+        seen.add(lid)
+        wg, rbl = lid % wg_per_rb, lid // wg_per_rb
         l, rb = rbl // nrb, rbl % nrb
         assert l < L
         cb0 = wg * TILES

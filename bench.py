@@ -41,7 +41,13 @@ if ROOT not in sys.path:
 
 import synth  # noqa: E402
 
-METRIC = "µs/call and achieved HBM GB/s (% of peak) for NVFP4 GEMV 7168×16384×1"
+def metric_for(M: int, K: int, L: int) -> str:
+    """The headline metric's wording, for the workload's shape (the headline
+    7168×16384×1 gives exactly the headline metric)."""
+    return f"µs/call and achieved HBM GB/s (% of peak) for NVFP4 GEMV {M}×{K}×{L}"
+
+
+METRIC = metric_for(7168, 16384, 1)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 512 * 2 ** 20
 WORKLOADS = {"headline": synth.HEADLINE, "balanced": synth.BALANCED, "batched": synth.BATCHED,
@@ -402,7 +408,7 @@ def main():
     achieved = ideal / (ms_per_step * 1e-3) / 1e9     # average launch over the timed region
     traffic = traffic_from_profile(w.name, layout)
     out = {
-        "metric": METRIC,
+        "metric": metric_for(M, K, L),
         "value": round(value_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,

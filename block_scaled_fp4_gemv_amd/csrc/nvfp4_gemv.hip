@@ -88,6 +88,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
 constexpr int kCachePolicyNT = 2;         // buffer load cache policy: non-temporal
 constexpr int64_t kMaxK = INT64_C(1) << 22; // keeps one workgroup's A offsets below 2^31
+constexpr int kRowThreads = 256;          // row kernel: 4 waves, one row each
+constexpr int kRowMaxCpl = 2;             // row kernel: chunks per lane, so K <= 64 * 2 * 32 = 4096
+constexpr int64_t kRowMaxSlots = 256;     // row kernel when the slots of all batches fit one per CU,
+constexpr int64_t kRowMaxSlotsShortK = 1024; // or four per CU with K <= 256
 
 static_assert(kPrefetch % kCpl == 0, "a row's chunk-steps must not straddle the prefetch ring");
 static_assert(kDeferRounds % (kPrefetch / kCpl) == 0, "deferred rounds end on a ring boundary");
@@ -709,6 +713,72 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     }
 }
 
+// Row kernel for small problems: one wave per row, every load of the row
+// issued at once. The main kernel's start-up (kernel-argument read, b's
+// inputs, then the staged scales, each behind a barrier) takes about three
+// memory round trips before the first result; a workgroup of a few rows pays
+// it whole. Here a workgroup of 4 waves owns one slot (the 4 rows that share
+// the blocked scale lines) and each wave one row. Lane j takes the chunks
+// j, j+64, ... (CPL of them, K <= 64*CPL*32, short K only): it loads their B chunks, SFB
+// pairs, SFA pairs and A chunks together, waits once, forms b', the exact
+// block sums and the scaled row sum as the main kernel does, and the wave's
+// lanes are summed with DPP. No LDS, no barrier, one memory round trip.
+template <int LAYOUT, int CPL>
+__global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_row_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
+    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, Params p)
+{
+    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t slot = (int32_t)(lid % (uint32_t)p.ns), l = (int32_t)(lid / (uint32_t)p.ns);
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int32_t lane = (int32_t)threadIdx.x & 63;
+    const int32_t r = ((slot >> 5) << 7) + (wave << 5) + (slot & 31);   // sub-row `wave` of the slot
+    if (r >= p.M)                                                       // wave-uniform; no barrier follows
+        return;
+    const int32_t nchunks = p.K >> 5, nkb = p.K >> 4, ncb = (nkb + 3) >> 2;
+    const uint8_t *a_r = A + (int64_t)l * p.a_batch + (int64_t)r * p.a_row;
+    const uint8_t *b_l = B + (int64_t)l * p.b_batch;
+    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
+    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+    int32_t cc[CPL];
+    bool live[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int32_t c = lane + 64 * i;
+        live[i] = c < nchunks;
+        cc[i] = min(c, nchunks - 1);                                    // clamped: every load is real
+    }
+    uint4_t bq[CPL], aq[CPL];
+    uint32_t sb[CPL], sa[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        bq[i] = *(const uint4_t *)(b_l + (int64_t)cc[i] * 16);
+        sb[i] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, cc[i], nkb, ncb));
+        sa[i] = LAYOUT == NVFP4_SF_PLAIN ? *(const uint16_t *)(sfa_l + (int64_t)r * p.sfa_row + 2 * cc[i])
+                                         : *(const uint16_t *)(sfa_l + sf_pair_offset<LAYOUT>(r, cc[i], nkb, ncb));
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        aq[i] = __builtin_nontemporal_load((const uint4_t *)(a_r + (int64_t)cc[i] * 16));
+    // every load above is issued before any use (the scheduler would otherwise
+    // trade registers for a second and third round trip)
+    __builtin_amdgcn_sched_barrier(0);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        uint4_t bp[4];
+        make_bprime(bq[i], sb[i], bp);
+        const float lo = dot_block(aq[i].x, aq[i].y, bp[0], bp[1]);
+        const float hi = dot_block(aq[i].z, aq[i].w, bp[2], bp[3]);
+        const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sa[i], false);
+        const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc));
+        acc = live[i] ? nacc : acc;
+    }
+    const float v = group_sum<64>(acc);
+    if (lane == 63)
+        C[(int64_t)l * p.c_batch + r] = f16_bits(v * p.alpha);
+}
+
 // ------------------------------------------------------------------ host side
 
 struct Plan {
@@ -723,6 +793,7 @@ struct Plan {
     int bfirst;           // b's inputs before the first ring of A (few row rounds per workgroup)
     int ilv;              // deferred rounds finished one per following round
     int nv;               // right-hand vectors (1 for the GEMV)
+    int row_cpl;          // > 0: the row kernel with this many chunks per lane
     int64_t n_wg;
     int lds_bytes;
     size_t ws_partials;   // bytes of float32 partials (after the ticket region)
@@ -854,6 +925,24 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
     pl.spw = (int)spw;
     pl.P = (int)cdiv(pl.ns, spw);
     pl.n_wg = (int64_t)pl.P * L * S;
+    if (nv == 1 && S == 1 && nchunks <= 64 * kRowMaxCpl &&
+        (total_slots <= kRowMaxSlots || (nchunks <= 8 && total_slots <= kRowMaxSlotsShortK))) {
+        // few rows and short K: one wave per row and one memory round trip
+        // (row kernel). Measured against the main kernel: 1000x4096x1 3.79 ->
+        // 3.13 us, 127x4096x3 3.98 -> 3.04, 128x256x1 3.59 -> 2.11, 1000x64x3
+        // 3.55 -> 2.58. With K = 16384 its blocked scale-pair loads (one 2-byte
+        // pair per lane, 32 lines per wave-wide load) made it slower (896x16384x1
+        // 4.86 -> 5.96 us), and so did 750 workgroups of 1000x4096x3 (4.43 -> 4.94).
+        pl.row_cpl = pow2_ceil(cdiv(nchunks, 64));
+        pl.spw = 1;
+        pl.P = pl.ns;
+        pl.n_wg = L * pl.ns;
+        pl.lpr = 64;
+        pl.stage_bytes = 0;
+        pl.lds_bytes = 0;
+        pl.bfirst = pl.ilv = 0;
+        return pl;
+    }
     pl.stage_bytes = stage_bytes(pl.lpr, spw);
     pl.lds_bytes = (int)lds_of(spw);
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
@@ -918,6 +1007,24 @@ hipError_t launch_layout(const Plan &pl, const void *a, const void *b, const voi
     case 4: return launch_lpr<LAYOUT, 4, NV>(pl, a, b, sfa, sfb, c, p, st);
     case 2: return launch_lpr<LAYOUT, 2, NV>(pl, a, b, sfa, sfb, c, p, st);
     default: return launch_lpr<LAYOUT, 1, NV>(pl, a, b, sfa, sfb, c, p, st);
+    }
+}
+
+template <int LAYOUT>
+hipError_t launch_row(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb, void *c,
+                      const Params &p, hipStream_t st)
+{
+    const dim3 grid((uint32_t)pl.n_wg), block(kRowThreads);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
+                           (const uint8_t *)sfb, (uint16_t *)c, p);
+        return hipGetLastError();
+    };
+    switch (pl.row_cpl) {
+    case 1: return go(nvfp4_gemv_row_kernel<LAYOUT, 1>);
+    case 2: return go(nvfp4_gemv_row_kernel<LAYOUT, 2>);
+    case 4: return go(nvfp4_gemv_row_kernel<LAYOUT, 4>);
+    default: return go(nvfp4_gemv_row_kernel<LAYOUT, 8>);
     }
 }
 
@@ -1003,7 +1110,10 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
         p.partials = (float *)((char *)ws + kCounterBytes);
     }
     hipError_t e;
-    if (pl.nv == 2) {
+    if (pl.row_cpl > 0) {
+        e = sf_layout == NVFP4_SF_PLAIN ? launch_row<NVFP4_SF_PLAIN>(pl, a, b, sfa, sfb, c, p, st)
+                                        : launch_row<NVFP4_SF_BLOCKED>(pl, a, b, sfa, sfb, c, p, st);
+    } else if (pl.nv == 2) {
         // two vectors, dense: B [L][2][K/2], SFB per vector a row (plain) or
         // the next 16-byte line of each tile (blocked), C [L][2][M]
         p.b_vec = K / 2;
@@ -1269,7 +1379,7 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
     plan->k_splits = pl.S;
     plan->k_per_split = pl.kc_split * 32;
     plan->workgroups = pl.n_wg;
-    plan->threads_per_wg = kBlock;
+    plan->threads_per_wg = pl.row_cpl > 0 ? kRowThreads : kBlock;
     plan->lds_bytes = pl.lds_bytes;
     return NVFP4_OK;
 }

@@ -137,7 +137,25 @@ def test_plans(w):
     tiles = synth.ceil_div(ns, p["rows_per_wg"] // 4)
     assert p["workgroups"] == tiles * w.L * p["k_splits"]
     assert p["lds_bytes"] <= 159 * 1024       # a workgroup fits the CU's 160 KiB of LDS
-    assert p["threads_per_wg"] == 320          # 4 computing waves and the staging wave
+    if w.K <= 4096 and (ns * w.L <= 256 or (w.K <= 256 and ns * w.L <= 1024)):
+        # few rows: the row kernel, 4 waves of one row each, one slot per workgroup, no LDS
+        assert p["threads_per_wg"] == 256 and p["rows_per_wg"] == 4 and p["lds_bytes"] == 0
+        assert p["lanes_per_row"] == 64
+    else:
+        assert p["threads_per_wg"] == 320      # 4 computing waves and the staging wave
+
+
+def test_row_kernel_boundaries():
+    """The row kernel takes K <= 4096 when the slots of all batches fit one
+    workgroup per CU (four per CU with K <= 256); larger shapes, longer K and
+    K-splits keep the main kernel."""
+    row = lambda M, K, L: g.nvfp4_gemv_plan(M, K, L)["threads_per_wg"] == 256
+    assert row(1024, 4096, 1) and not row(1025, 4096, 1)          # 256 slots; 257
+    assert row(127, 4096, 3) and row(128, 256, 2) and row(1000, 64, 3) and row(4096, 256, 1)
+    assert not row(4097, 256, 1) and not row(1000, 288, 3)        # 1025 slots; K above 256 with 750
+    assert not row(7168, 16384, 1) and not row(1000, 4096, 3) and not row(896, 16384, 1)
+    assert not row(127, 4128, 1)                                  # K above 64 lanes x 2 chunks
+    assert not row(5, 32768, 1)                                   # long K (split)
 
 
 def test_long_k_is_segmented_not_split():

@@ -206,8 +206,9 @@ def test_batch_slices_match_single_batch_calls():
         ref = oracle.gemv(one, "blocked")
         assert oracle.check(got, ref).all()
         pa, pb = g.nvfp4_gemv_plan(1000, 4096, 3), g.nvfp4_gemv_plan(1000, 4096, 1)
-        if pa["k_splits"] == pb["k_splits"] == 1:
-            assert bits_equal(got[0], full[l])
+        same_kernel = all(pa[k] == pb[k] for k in ("threads_per_wg", "lanes_per_row"))
+        if pa["k_splits"] == pb["k_splits"] == 1 and same_kernel:
+            assert bits_equal(got[0], full[l])      # same per-row summation order
         else:
             assert oracle.check(full[l:l + 1], ref).all()
 

@@ -22,6 +22,7 @@ import synth
 
 THREADS, CPL, PREFETCH, XCDS, MAX_TICKETS = 256, 4, 8, 8, 1024
 LOADER = 64                 # threads of the staging wave
+ROW_THREADS = 256           # the row kernel for small problems (4 waves, one row each)
 DMA_BYTES = 64 * 16         # LDS bytes one wave-wide staging load fills
 STAGE_B = True              # blocked layout: the staging wave stages B as well as SFB
 
@@ -60,6 +61,70 @@ def sf_offset(layout, r, kb, nkb, ncb):
     return ((r >> 7) * ncb + (kb >> 2)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (kb & 3)
 
 
+def check_row_shape(M, K, L, layout, p, ws_bytes, strides=None):
+    """The row kernel (small problems): a workgroup of 4 waves owns one slot,
+    wave w its sub-row w; lane j loads chunks j, j+64, ... (clamped), their B
+    chunks, SFB pairs and SFA pairs; lane 63 writes the row's output."""
+    nchunks, nkb = K // 32, K // 16
+    ncb = cdiv(nkb, 4)
+    ns = 32 * (M // 128) + min(32, M % 128)
+    assert p["workgroups"] == L * ns and p["rows_per_wg"] == 4 and p["k_splits"] == 1
+    assert p["lds_bytes"] == 0 and ws_bytes == 0
+    assert nchunks <= 64 * 2 and (L * ns <= 256 or (nchunks <= 8 and L * ns <= 1024))
+    cpl = 1
+    while 64 * cpl < nchunks:
+        cpl *= 2
+    sd = strides or g.nvfp4_gemv_dense_strides(M, K, L, layout)
+    a_row, a_bat, b_bat, c_bat = sd["a_row"], sd["a_batch"], sd["b_batch"], sd["c_batch"]
+    sfa_row, sfa_bat, sfb_bat = sd["sfa_row"], sd["sfa_batch"], sd["sfb_batch"]
+    a_bytes = (L - 1) * a_bat + (M - 1) * a_row + K // 2
+    b_size = (L - 1) * b_bat + K // 2
+    sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512
+    sfb_batch = nkb if layout == 0 else ncb * 512
+    sfa_size = (L - 1) * sfa_bat + ((M - 1) * sfa_row + nkb if layout == 0 else sfa_batch)
+    sfb_size = (L - 1) * sfb_bat + sfb_batch
+    n_wg = p["workgroups"]
+    lids = xcd_remap(np.arange(n_wg), n_wg)
+    assert np.array_equal(np.sort(lids), np.arange(n_wg)), "remap is not a bijection"
+    lane = np.arange(64)
+    written = np.zeros((L - 1) * c_bat + M, np.int64)
+    taken = np.zeros((L, M, nchunks), np.int64)
+    for lid in lids:
+        slot, l = lid % ns, lid // ns
+        assert l < L
+        for w in range(4):
+            r = ((slot >> 5) << 7) + (w << 5) + (slot & 31)
+            if r >= M:
+                continue
+            for i in range(cpl):
+                c = lane + 64 * i
+                live = c < nchunks
+                cc = np.minimum(c, nchunks - 1)
+                a_off = l * a_bat + r * a_row + cc * 16
+                assert a_off.min() >= 0 and (a_off + 16).max() <= a_bytes, "A read outside the tensor"
+                b_off = l * b_bat + cc * 16
+                assert b_off.min() >= 0 and (b_off + 16).max() <= b_size, "B read outside the tensor"
+                sb = l * sfb_bat + sf_offset(layout, np.zeros_like(cc), 2 * cc, nkb, ncb)
+                assert sb.min() >= 0 and (sb + 2).max() <= sfb_size and (sb % 2 == 0).all()
+                if layout == 0:
+                    sa = l * sfa_bat + r * sfa_row + 2 * cc
+                else:
+                    sa = l * sfa_bat + sf_offset(1, np.full_like(cc, r), 2 * cc, nkb, ncb)
+                assert sa.min() >= 0 and (sa + 2).max() <= sfa_size and (sa % 2 == 0).all()
+                # the pair is scales (r, 2c) and (r, 2c+1)
+                for b in range(2):
+                    want = l * sfa_bat + (r * sfa_row + 2 * cc + b if layout == 0
+                                          else sf_offset(1, np.full_like(cc, r), 2 * cc + b, nkb, ncb))
+                    assert np.array_equal(sa + b, want), "SFA pair is not the chunk's two scales"
+                np.add.at(taken, (l, r, cc[live]), 1)
+            written[l * c_bat + r] += 1
+    assert (taken == 1).all(), "some (row, chunk) is taken zero or several times"
+    expect = np.zeros_like(written)
+    for l in range(L):
+        expect[l * c_bat + np.arange(M)] += 1
+    assert np.array_equal(written, expect), "some output row is written zero or several times"
+
+
 def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREADS, cpl=CPL,
                 prefetch=PREFETCH, max_tickets=MAX_TICKETS, strides=None):
     """Walk the whole grid of one launch. ``plan``/``workspace_bytes`` default
@@ -68,6 +133,8 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     THREADS, CPL, PREFETCH = threads, cpl, prefetch
     p = (plan or g.nvfp4_gemv_plan)(M, K, L)
     ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
+    if p["threads_per_wg"] == ROW_THREADS:
+        return check_row_shape(M, K, L, layout, p, ws_bytes, strides)
     lpr, spw, S = p["lanes_per_row"], p["rows_per_wg"] // 4, p["k_splits"]
     kc, n_wg, lds_bytes = p["k_per_split"] // 32, p["workgroups"], p["lds_bytes"]
     assert p["threads_per_wg"] == THREADS + LOADER

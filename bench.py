@@ -238,7 +238,7 @@ def bench_small_n(args, w, dev):
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"small_n{N}_{w.name}", "M": M, "N": N, "K": K, "L": L, "sf_layout": layout,
-                   "ideal_bytes_per_call": ideal, "plan": g.nvfp4_gemm_small_n_plan(M, N, K, L)},
+                   "ideal_bytes_per_call": ideal, "plan": g.nvfp4_gemm_small_n_plan(M, N, K, L, layout)},
         "us_per_call": round(ms * 1e3, 3), "verified_vs_oracle": verified,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}), flush=True)

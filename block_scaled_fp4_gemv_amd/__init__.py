@@ -125,7 +125,7 @@ def lib():
     L.nvfp4_gemm_small_n.restype = i32
     L.nvfp4_gemm_small_n.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.c_float, vp]
     L.nvfp4_gemm_small_n_plan.restype = i32
-    L.nvfp4_gemm_small_n_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int32),
+    L.nvfp4_gemm_small_n_plan.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]
     L.nvfp4_scales_to_blocked.restype = i32
     L.nvfp4_scales_to_blocked.argtypes = [vp, vp, i64, i64, i64, vp]
@@ -300,9 +300,10 @@ def nvfp4_gemv_plan(M: int, K: int, L: int) -> dict:
     return plan.as_dict()
 
 
-def nvfp4_gemm_small_n_plan(M: int, N: int, K: int, L: int) -> dict:
+def nvfp4_gemm_small_n_plan(M: int, N: int, K: int, L: int, layout="blocked") -> dict:
     r, wg, lds = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
-    st = lib().nvfp4_gemm_small_n_plan(M, N, K, L, ctypes.byref(r), ctypes.byref(wg), ctypes.byref(lds))
+    st = lib().nvfp4_gemm_small_n_plan(M, N, K, L, layout_id(layout), ctypes.byref(r), ctypes.byref(wg),
+                                       ctypes.byref(lds))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemm_small_n_plan")
     return {"rows_per_wg": r.value, "workgroups": wg.value, "lds_bytes": lds.value}

@@ -70,10 +70,10 @@ __device__ inline int64_t sn_pair_offset(int64_t r, int32_t c, int32_t nkb, int3
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// Matrix-core kernel. A wave owns kMfRT tiles of 16 rows and a contiguous
-// share of the K-steps (one step = 4 chunks, 128 k); the kMfWaves waves of a
-// workgroup split K between them and their partial tiles are added in LDS in
-// a fixed order. In a step, lane group g (lanes 16g .. 16g+15) takes chunk g:
+// Matrix-core kernel. A wave owns kMfRT tiles of 16 rows and every
+// kMfWaves-th group of kMfGroup K-steps (one step = 4 chunks, 128 k), so the
+// kMfWaves waves of a workgroup read neighbouring pieces of the same rows at
+// the same time; their partial tiles are added in LDS in a fixed order. In a step, lane group g (lanes 16g .. 16g+15) takes chunk g:
 // lane i of the group holds 16 bytes of row i of each tile (the MFMA's A
 // operand, k split into four runs of 8) and the same chunk of vector i (its B
 // operand; zero for i >= N). The 16x16 result has lane L holding rows
@@ -83,6 +83,7 @@ constexpr int kMfRT = 2;                      // 16-row tiles per wave
 constexpr int kMfWaves = 4;                   // waves per workgroup, splitting K
 constexpr int kMfThreads = 64 * kMfWaves;
 constexpr int kMfRing = 4;                    // K-steps of loads in flight per lane
+constexpr int kMfGroup = 1;                   // consecutive K-steps a wave takes in turn (a power of 2)
 
 struct MfParams {
     int32_t M, K, L, N;
@@ -106,8 +107,12 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);        // wave-uniform: scalar loop bounds
     const int grp = lane >> 4, i16 = lane & 15;
     const int32_t r0 = tile * (16 * kMfRT);
-    const int32_t s_begin = (int32_t)((int64_t)wave * nfull / kMfWaves);
-    const int32_t s_end = (int32_t)((int64_t)(wave + 1) * nfull / kMfWaves);
+    // the wave's local steps u = 0 .. nu-1 are the K-steps
+    // (u / kMfGroup) * kMfWaves * kMfGroup + wave * kMfGroup + u % kMfGroup
+    constexpr int32_t kSpan = kMfWaves * kMfGroup;
+    const int32_t ncyc = nfull / kSpan;
+    const int32_t nu = ncyc * kMfGroup + min(max(nfull - ncyc * kSpan - wave * kMfGroup, 0), kMfGroup);
+    const int32_t s_begin = 0, s_end = nu;
     const int64_t row_bytes = K >> 1;
     // step s of chunk column grp: A and B move by 64 bytes, a scale pair by
     // 8 bytes (plain) or two 512-byte tiles (blocked; the pair's place in the
@@ -160,7 +165,8 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
         // with the default cache policy: a step takes 64 of a row's 128-byte
         // line and the next step the other 64, which then hits L2 (with
         // non-temporal loads about 5% of the lines were fetched twice)
-        auto load_step = [&](int32_t s, int slot) {
+        auto load_step = [&](int32_t u, int slot) {
+            const int32_t s = (u / kMfGroup) * kSpan + wave * kMfGroup + u % kMfGroup;
             const int64_t ao = (int64_t)s * 64, so = (int64_t)s * kSfStep;
 #pragma unroll
             for (int t = 0; t < kMfRT; ++t) {
@@ -242,6 +248,283 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
 #pragma unroll
             for (int w = 0; w < kMfWaves; ++w)
                 v += ((const float *)&mf_part[w][t][ln])[j];
+            C[((int64_t)l * N + col) * M + row] = f16_bits(v * p.alpha);
+        }
+    }
+}
+
+// Staged matrix-core kernel (blocked scales; N >= 3 where B, the SFB pairs
+// and the workgroup's SFA lines fit in LDS). Same MFMA layout as above, but
+// only A is read from global memory in the loop: per-step loads of the scale
+// pairs and of B (a few bytes per lane, touching several lines each) took
+// about a third of the streaming time. A prologue stages all of B, the SFB
+// dwords and the workgroup's SFA lines into LDS (direct-to-LDS copies for B
+// and SFA), issued right after the first ring of A.
+//
+// Rows. A blocked scale tile is 128 rows x 4 blocks; its 16-byte piece p holds
+// the 4 blocks of rows p, p+32, p+64, p+96. Workgroup h (0..3) of a 128-row
+// block takes the pieces 8h .. 8h+7, i.e. the 32 rows 8h + p' + 32j (p' < 8,
+// j < 4), so its SFA is one whole 128-byte line per tile and no line is
+// shared. MFMA row m (0..15) of tile t is row 8h + (m & 7) + 32 (2 (m >> 3) + t):
+// one 8-byte LDS read then gives a lane the 4 blocks of its row in both tiles.
+constexpr int kMsWgPerBlock = 4;              // workgroups per 128-row block
+constexpr int kMsDmaBytes = 64 * 16;          // LDS bytes one wave-wide direct-to-LDS copy fills
+constexpr int kMsMaxNcb = kMfThreads;         // 4-block groups (K / 64) the SFB staging covers: one per lane
+constexpr int kMsMaxDmaPerWave = 40;          // direct-to-LDS copies per wave (the wait counter holds 63)
+constexpr int64_t kMsLdsLimit = 150 * 1024;     // dynamic LDS; the static partial tiles take 8 KiB more
+
+struct MsLayout {
+    int32_t b_vec;                            // LDS bytes per staged vector of B (16 more than its copies fill)
+    int32_t sfb_vec;                          // LDS bytes per vector of staged SFB dwords
+    int32_t b_bytes, sfa_bytes, sfb_bytes;    // LDS regions, in this order
+    int32_t n_dma_b, n_dma_sfa;               // wave-wide copies per vector of B, and of SFA
+};
+
+// LDS layout: vector n of B at n * b_vec (chunk c at +16 c; b_vec = 16 mod 128,
+// so the vectors' chunks fall in different banks), the SFA line of 4-block
+// group q at sfa + q * 128, the SFB dword (n, q) at sfb + n * sfb_vec + 4 q
+// (sfb_vec / 4 = 2 mod 32).
+__host__ __device__ inline MsLayout ms_layout(int32_t K, int32_t N)
+{
+    const int32_t nchunks = K >> 5, ncb = ((K >> 4) + 3) >> 2;
+    MsLayout o;
+    o.n_dma_b = (nchunks + 63) / 64;
+    o.n_dma_sfa = (ncb * 8 + 63) / 64;
+    o.b_vec = o.n_dma_b * kMsDmaBytes + 16;
+    o.sfb_vec = (ncb * 4 + 127) / 128 * 128 + 8;
+    o.b_bytes = (N * o.b_vec + 127) / 128 * 128;
+    o.sfa_bytes = o.n_dma_sfa * kMsDmaBytes;
+    o.sfb_bytes = N * o.sfb_vec;
+    return o;
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_dst + lane*16
+// (global_load_lds_dwordx4, LDS address from M0). Inline assembly, so the
+// compiler does not track the copy: the prologue waits for the copies itself.
+// Nothing else in this file uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __attribute__((always_inline)) inline void ms_copy16(const void *src, const uint8_t *lds_dst)
+{
+    const uint32_t addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(K0), other counters unconstrained
+template <int K0>
+__device__ __attribute__((always_inline)) inline void ms_wait_vmcnt()
+{
+    static_assert(K0 >= 0 && K0 < 64, "vmcnt holds 0..63");
+    __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xC00F) | (K0 & 15) | ((K0 >> 4) << 14));
+}
+
+__global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_staged_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
+    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, MfParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t ms_lds[];
+    __shared__ float4_t ms_part[kMfWaves][kMfRT][64];
+    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t wgb = (int32_t)(lid % (uint32_t)p.P), l = (int32_t)(lid / (uint32_t)p.P);
+    const int32_t blk = wgb / kMsWgPerBlock, h = wgb % kMsWgPerBlock;
+    const int32_t M = p.M, K = p.K, N = p.N;
+    const int32_t nchunks = K >> 5, ncb = ((K >> 4) + 3) >> 2;
+    const int32_t nfull = nchunks >> 2;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, i16 = lane & 15;
+    const int64_t row_bytes = K >> 1;
+    const MsLayout lay = ms_layout(K, N);
+    uint8_t *const sB = ms_lds;
+    uint8_t *const sSFA = ms_lds + lay.b_bytes;
+    uint8_t *const sSFB = sSFA + lay.sfa_bytes;
+    const int32_t rbase = blk * 128 + 8 * h;                          // row of p' = 0, j = 0
+
+    const uint8_t *b_l = B + (int64_t)l * N * row_bytes;
+    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
+    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+
+    // the wave's local steps u = 0 .. nu-1 are the K-steps u * kMfWaves + wave
+    const int32_t nu = nfull / kMfWaves + (wave < nfull % kMfWaves ? 1 : 0);
+    const uint8_t *a_ptr[kMfRT];
+#pragma unroll
+    for (int t = 0; t < kMfRT; ++t) {
+        const int32_t r = min(rbase + (i16 & 7) + 32 * (2 * (i16 >> 3) + t), M - 1);
+        a_ptr[t] = A + ((int64_t)l * M + r) * row_bytes + grp * 16 + (int64_t)wave * 64;
+    }
+
+    // prologue, in issue order: the first ring of A, the copies of B and of
+    // the SFA lines, the SFB dwords into registers
+    uint4_t abuf[kMfRing][kMfRT];
+    auto load_step = [&](int32_t u, int slot) {
+        const int64_t ao = (int64_t)u * (64 * kMfWaves);
+#pragma unroll
+        for (int t = 0; t < kMfRT; ++t)
+            abuf[slot][t] = *(const uint4_t *)(a_ptr[t] + ao);
+    };
+#pragma unroll
+    for (int d = 0; d < kMfRing; ++d) {
+        if (d < nu)
+            load_step(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int32_t nv = 0; nv < N; ++nv)
+        for (int32_t i = wave; i < lay.n_dma_b; i += kMfWaves)
+            ms_copy16(b_l + (int64_t)nv * row_bytes + (int64_t)min(i * 64 + lane, nchunks - 1) * 16,
+                      sB + nv * lay.b_vec + i * kMsDmaBytes);
+    for (int32_t i = wave; i < lay.n_dma_sfa; i += kMfWaves) {
+        const int32_t it = min(i * 64 + lane, ncb * 8 - 1);           // past the end: clamped, never read
+        ms_copy16(sfa_l + ((int64_t)blk * ncb + (it >> 3)) * 512 + (8 * h + (it & 7)) * 16, sSFA + i * kMsDmaBytes);
+    }
+    // SFB of vector nv, 4-block group q = tid: rows nv < 8 of the first tile row
+    uint32_t sfb_v[kSnMaxN];
+    const int32_t qs = min(tid, ncb - 1);
+#pragma unroll
+    for (int nv = 0; nv < kSnMaxN; ++nv)
+        sfb_v[nv] = *(const uint32_t *)(sfb_l + (int64_t)qs * 512 + min(nv, N - 1) * 16);
+    ms_wait_vmcnt<0>();                                               // this wave's copies have landed
+    if (tid < ncb) {
+#pragma unroll
+        for (int nv = 0; nv < kSnMaxN; ++nv)
+            if (nv < N)
+                *(uint32_t *)(sSFB + nv * lay.sfb_vec + tid * 4) = sfb_v[nv];
+    }
+    __syncthreads();                                                  // B, SFB and SFA are staged
+
+    float4_t acc[kMfRT];
+#pragma unroll
+    for (int t = 0; t < kMfRT; ++t)
+        acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int32_t n = min(i16, N - 1);
+    const bool n_live = i16 < N;
+    // LDS addresses of step s = 0 for this lane; a step moves them by
+    // 64 (B), 8 (SFB) and 256 (SFA) bytes
+    const uint8_t *lb = sB + n * lay.b_vec + grp * 16;
+    const uint8_t *lsb = sSFB + n * lay.sfb_vec + 2 * grp;
+    const uint8_t *lsa = sSFA + (grp >> 1) * 128 + (i16 & 7) * 16 + 8 * (i16 >> 3);
+    const int sa_shift = 16 * (grp & 1);
+
+    // the staged operands of the wave's local step u (clamped to its last
+    // step, so that a read ahead past the end stays on real data)
+    struct Staged {
+        uint4_t b;
+        uint32_t sb;
+        uint2_t sa2;
+    };
+    auto read_staged = [&](int32_t u) {
+        const int32_t s = min(u, nu - 1) * kMfWaves + wave;
+        Staged o;
+        o.b = *(const uint4_t *)(lb + s * 64);
+        o.sb = *(const uint16_t *)(lsb + s * 8);                      // a slot past N is zeroed at use
+        o.sa2 = *(const uint2_t *)(lsa + s * 256);
+        return o;
+    };
+    // one step from the ring slot's A and the staged operands
+    auto mma_step = [&](const uint4_t (&araw)[kMfRT], const Staged &st) {
+        uint4_t bp[4];
+        make_bprime(st.b, n_live ? st.sb : 0u, bp);
+#pragma unroll
+        for (int t = 0; t < kMfRT; ++t) {
+            const uint32_t sa = ((t == 0 ? st.sa2.x : st.sa2.y) >> sa_shift) & 0xFFFFu;
+            uint4_t ap[4];
+            make_bprime(araw[t], sa, ap);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap[q]),
+                                                                __builtin_bit_cast(half8_t, bp[q]), acc[t], 0, 0,
+                                                                0);
+        }
+    };
+
+    if (nu > 0) {
+        // as in the kernel above: whole rings with unconditional refills, the
+        // last ring refilled only up to nu, then the steps still in the ring.
+        // The staged operands are read one step ahead, so that their LDS
+        // latency hides behind the current step's work.
+        Staged cur = read_staged(0);
+        int32_t u0 = 0;
+        for (; u0 + 2 * kMfRing <= nu; u0 += kMfRing) {
+#pragma unroll
+            for (int d = 0; d < kMfRing; ++d) {
+                const Staged nxt = read_staged(u0 + d + 1);
+                __builtin_amdgcn_sched_barrier(0);                     // issue the reads ahead of the step
+                mma_step(abuf[d], cur);
+                cur = nxt;
+                __builtin_amdgcn_sched_barrier(0);
+                load_step(u0 + d + kMfRing, d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < kMfRing; ++d) {
+            if (u0 + d < nu) {
+                const Staged nxt = read_staged(u0 + d + 1);
+                __builtin_amdgcn_sched_barrier(0);                     // issue the reads ahead of the step
+                mma_step(abuf[d], cur);
+                cur = nxt;
+                __builtin_amdgcn_sched_barrier(0);
+                if (u0 + d + kMfRing < nu)
+                    load_step(u0 + d + kMfRing, d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        u0 += kMfRing;
+#pragma unroll
+        for (int d = 0; d < kMfRing; ++d)
+            if (u0 + d < nu) {
+                const Staged nxt = read_staged(u0 + d + 1);
+                __builtin_amdgcn_sched_barrier(0);                     // issue the reads ahead of the step
+                mma_step(abuf[d], cur);
+                cur = nxt;
+            }
+    }
+
+    // the ragged last step (K not a multiple of 128), taken by the last wave:
+    // chunks past K read chunk nchunks-1 and get zero scale pairs
+    if ((nchunks & 3) != 0 && wave == kMfWaves - 1) {
+        const int32_t c = min(4 * nfull + grp, nchunks - 1);
+        const bool live = 4 * nfull + grp < nchunks;
+        uint4_t araw[kMfRT];
+#pragma unroll
+        for (int t = 0; t < kMfRT; ++t)
+            araw[t] = *(const uint4_t *)(a_ptr[t] - grp * 16 - (int64_t)wave * 64 + (int64_t)c * 16);
+        // staged operands of chunk c: the lane's step-0 addresses are for
+        // chunk grp, so move them to chunk c by hand
+        const uint4_t braw = *(const uint4_t *)(sB + n * lay.b_vec + c * 16);
+        const uint32_t sb = (live && n_live) ? (uint32_t) * (const uint16_t *)(sSFB + n * lay.sfb_vec + 2 * c) : 0u;
+        const uint2_t sa2 = *(const uint2_t *)(sSFA + (c >> 1) * 128 + (i16 & 7) * 16 + 8 * (i16 >> 3));
+        const int sh = 16 * (c & 1);
+        uint4_t bp[4];
+        make_bprime(braw, sb, bp);
+#pragma unroll
+        for (int t = 0; t < kMfRT; ++t) {
+            const uint32_t sa = live ? ((t == 0 ? sa2.x : sa2.y) >> sh) & 0xFFFFu : 0u;
+            uint4_t ap[4];
+            make_bprime(araw[t], sa, ap);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap[q]),
+                                                                __builtin_bit_cast(half8_t, bp[q]), acc[t], 0, 0,
+                                                                0);
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < kMfRT; ++t)
+        ms_part[wave][t][lane] = acc[t];
+    __syncthreads();
+    for (int e = tid; e < kMfRT * 64 * 4; e += kMfThreads) {
+        const int t = e >> 8, ln = (e >> 2) & 63, j = e & 3;
+        const int m = 4 * (ln >> 4) + j;                               // MFMA row of the result element
+        const int32_t col = ln & 15, row = rbase + (m & 7) + 32 * (2 * (m >> 3) + t);
+        if (col < N && row < M) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kMfWaves; ++w)
+                v += ((const float *)&ms_part[w][t][ln])[j];
             C[((int64_t)l * N + col) * M + row] = f16_bits(v * p.alpha);
         }
     }
@@ -403,18 +686,58 @@ hipError_t mf_launch(int64_t grid, const void *a, const void *b, const void *sfa
     return hipGetLastError();
 }
 
+// The staged kernel's LDS bytes for (M, N, K, L), or -1 where it does not
+// apply: N >= 3, LDS within the limit, each wave's copies within what the
+// wait counter holds next to the ring and the SFB loads, one 4-block group of
+// SFB per lane at most (K <= 16384).
+int64_t ms_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t L)
+{
+    if (N < kMfMinN || N > kSnMaxN)
+        return -1;
+    const MsLayout o = ms_layout((int32_t)K, (int32_t)N);
+    const int64_t bytes = (int64_t)o.b_bytes + o.sfa_bytes + o.sfb_bytes;
+    const int64_t ncb = (K / 16 + 3) / 4;
+    if (bytes > kMsLdsLimit ||
+        N * ((o.n_dma_b + kMfWaves - 1) / kMfWaves) + (o.n_dma_sfa + kMfWaves - 1) / kMfWaves > kMsMaxDmaPerWave ||
+        ncb > kMsMaxNcb || L * ((M + 127) / 128) * kMsWgPerBlock > INT32_MAX)
+        return -1;
+    return bytes;
+}
+
+hipError_t ms_launch(int64_t grid, int64_t lds, const void *a, const void *b, const void *sfa, const void *sfb,
+                     void *c, const MfParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL(nvfp4_gemm_small_n_mfma_staged_kernel, dim3((uint32_t)grid), dim3(kMfThreads),
+                       (uint32_t)lds, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
+                       (const uint8_t *)sfb, (uint16_t *)c, p);
+    return hipGetLastError();
+}
+
 bool sn_aligned(const void *q, uintptr_t a) { return ((uintptr_t)q & (a - 1)) == 0; }
 
 } // namespace
 
 extern "C" {
 
-nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t L, int32_t *rows_per_wg,
-                                       int64_t *workgroups, int32_t *lds_bytes)
+nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout,
+                                       int32_t *rows_per_wg, int64_t *workgroups, int32_t *lds_bytes)
 {
     if (M < 1 || N < 1 || N > kSnMaxN || L < 1 || K < 32 || K % 32 != 0 || K > (INT64_C(1) << 22) ||
         M > INT32_MAX / 2 || L > INT32_MAX / 2 || L * M > (INT64_C(1) << 62) / K)
         return NVFP4_ERR_INVALID_SHAPE;
+    if (sf_layout != NVFP4_SF_PLAIN && sf_layout != NVFP4_SF_BLOCKED)
+        return NVFP4_ERR_INVALID_LAYOUT;
+    const int64_t ms_lds = sf_layout == NVFP4_SF_BLOCKED ? ms_lds_bytes(M, N, K, L) : -1;
+    if (ms_lds >= 0) {
+        // the staged matrix-core kernel: 4 workgroups of 32 rows per 128-row block
+        if (rows_per_wg)
+            *rows_per_wg = (int32_t)std::min<int64_t>(32, M);
+        if (workgroups)
+            *workgroups = L * ((M + 127) / 128) * kMsWgPerBlock;
+        if (lds_bytes)
+            *lds_bytes = (int32_t)ms_lds;
+        return NVFP4_OK;
+    }
     if (N >= kMfMinN) {
         // the matrix-core kernel: one workgroup per kMfRT tiles of 16 rows, static LDS only
         const int64_t rows = 16 * kMfRT, P = (M + rows - 1) / rows;
@@ -455,11 +778,9 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
         return NVFP4_ERR_NULL_POINTER;
     int32_t R = 0, lds = 0;
     int64_t grid = 0;
-    nvfp4_status_t st = nvfp4_gemm_small_n_plan(M, N, K, L, &R, &grid, &lds);
+    nvfp4_status_t st = nvfp4_gemm_small_n_plan(M, N, K, L, sf_layout, &R, &grid, &lds);
     if (st != NVFP4_OK)
         return st;
-    if (sf_layout != NVFP4_SF_PLAIN && sf_layout != NVFP4_SF_BLOCKED)
-        return NVFP4_ERR_INVALID_LAYOUT;
     if (!sn_aligned(a, 16) || !sn_aligned(b, 16) || !sn_aligned(sfa, 16) || !sn_aligned(sfb, 4) ||
         !sn_aligned(c, 2))
         return NVFP4_ERR_MISALIGNED;
@@ -491,9 +812,13 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
         q.sfa_batch = sfa_batch;
         q.sfb_batch = sfb_batch;
         q.alpha = alpha;
-        e = sf_layout == NVFP4_SF_PLAIN
-                ? mf_launch<NVFP4_SF_PLAIN>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream)
-                : mf_launch<NVFP4_SF_BLOCKED>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream);
+        if (lds > 0) {
+            e = ms_launch(grid, lds, a, b, sfa, sfb, c, q, (hipStream_t)stream);
+        } else {
+            e = sf_layout == NVFP4_SF_PLAIN
+                    ? mf_launch<NVFP4_SF_PLAIN>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream)
+                    : mf_launch<NVFP4_SF_BLOCKED>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream);
+        }
     } else {
         SnParams p{};
         p.M = (int32_t)M;

@@ -242,13 +242,15 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
                                   void *c, int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout,
                                   float alpha, void *stream);
 
-/* Launch plan of nvfp4_gemm_small_n's own kernels for a shape: rows per
- * workgroup, workgroups (256 threads each) and dynamic LDS bytes (0 for the
- * matrix-core kernel of N >= 3, whose workgroups own 32 rows); any output
- * pointer may be NULL. Returns NVFP4_ERR_INVALID_SHAPE for shapes it does not
- * take. */
-nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t L, int32_t *rows_per_wg,
-                                       int64_t *workgroups, int32_t *lds_bytes);
+/* Launch plan of nvfp4_gemm_small_n's own kernels for a shape and scale
+ * layout: rows per workgroup, workgroups (256 threads each) and dynamic LDS
+ * bytes. From N = 3 the workgroups own 32 rows; with blocked scales, where B,
+ * the SFB pairs and a workgroup's SFA lines fit in LDS (K <= 16384), they are
+ * staged there (lds_bytes > 0) and each 128-row block has 4 workgroups. Any
+ * output pointer may be NULL. Returns NVFP4_ERR_INVALID_SHAPE for shapes it
+ * does not take, NVFP4_ERR_INVALID_LAYOUT for an unknown layout. */
+nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout,
+                                       int32_t *rows_per_wg, int64_t *workgroups, int32_t *lds_bytes);
 
 /*
  * Device-side reblocking of plain scale factors into the 128x4 blocked layout

@@ -293,13 +293,25 @@ def test_small_n_plan():
     assert p["workgroups"] == 256 and p["rows_per_wg"] == 28
     p = g.nvfp4_gemm_small_n_plan(100000, 2, 64, 1)
     assert p["lds_bytes"] <= 48 * 1024
-    # N >= 3: the matrix-core kernel, 32-row tiles per workgroup, static LDS only
-    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1)
+    # N >= 3, plain scales: the matrix-core kernel, 32-row tiles per workgroup, static LDS only
+    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1, "plain")
     assert p["workgroups"] == 224 and p["rows_per_wg"] == 32 and p["lds_bytes"] == 0
-    p = g.nvfp4_gemm_small_n_plan(7, 3, 96, 2)
+    p = g.nvfp4_gemm_small_n_plan(7, 3, 96, 2, "plain")
     assert p["workgroups"] == 2 and p["rows_per_wg"] == 7
+    # blocked scales: the staged kernel, 4 workgroups per 128-row block, B and the scales in LDS
+    p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1, "blocked")
+    assert p["workgroups"] == 224 and p["rows_per_wg"] == 32 and 0 < p["lds_bytes"] <= 150 * 1024
+    p = g.nvfp4_gemm_small_n_plan(7, 3, 96, 2, "blocked")
+    assert p["workgroups"] == 8 and p["rows_per_wg"] == 7 and p["lds_bytes"] > 0
+    p = g.nvfp4_gemm_small_n_plan(1000, 4, 4096, 3, "blocked")
+    assert p["workgroups"] == 3 * 8 * 4
+    # past K = 16384 the blocked scales take the unstaged kernel
+    p = g.nvfp4_gemm_small_n_plan(300, 4, 20480, 1, "blocked")
+    assert p["workgroups"] == 10 and p["lds_bytes"] == 0
     with pytest.raises(g.Nvfp4Error):
         g.nvfp4_gemm_small_n_plan(128, 9, 256, 1)
+    with pytest.raises(g.Nvfp4Error):
+        g.nvfp4_gemm_small_n_plan(128, 4, 256, 1, 7)
 
 
 def test_noalloc_validation_before_launch():

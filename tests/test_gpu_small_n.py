@@ -48,12 +48,14 @@ CASES = [(1, 1, 32, 1), (7, 3, 96, 2), (128, 2, 2048, 1), (300, 4, 20480, 2), (1
          # N = 2 through the GEMV kernel (ragged M, several batches, segmented K),
          # and N = 2 where a K-split is needed (the skinny kernel)
          (1000, 2, 4096, 3), (300, 2, 20480, 2), (127, 2, 16384, 1),
-         # register matrix-core kernel (K % 256 != 0) over many batches, ragged M and K
+         # matrix-core kernels over many batches, ragged M and K (a last step of
+         # fewer than 4 chunks; no whole step at all for K = 96); blocked scales
+         # with K <= 16384 take the staged kernel, plain scales and K > 16384 the
+         # unstaged one
          (300, 4, 1056, 120), (100, 8, 160, 300), (33, 3, 96, 5),
-         # staged matrix-core kernel (K % 256 == 0): partial last panels, one-tile
-         # workgroups, slots whose rows pass M, many batches
+         # 128-row blocks whose workgroups own no row below M, a single 4-block group
          (5, 3, 768, 2), (127, 5, 2304, 3), (300, 6, 4352, 1), (1, 8, 256, 1), (129, 7, 256, 2),
-         (1000, 4, 7168, 2), (128, 4, 1280, 5)]
+         (1000, 4, 7168, 2), (128, 4, 1280, 5), (20, 3, 64, 1), (7168, 3, 16384, 1)]
 
 
 @pytest.mark.parametrize("M,N,K,L", CASES)

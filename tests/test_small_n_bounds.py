@@ -30,7 +30,7 @@ def pair_offset(layout, r, c, nkb, ncb):
 
 
 def check(M, N, K, L, layout):
-    p = g.nvfp4_gemm_small_n_plan(M, N, K, L)
+    p = g.nvfp4_gemm_small_n_plan(M, N, K, L, layout)
     R, n_wg, lds = p["rows_per_wg"], p["workgroups"], p["lds_bytes"]
     assert lds == R * N * WAVES * 4 and lds <= 48 * 1024
     P = n_wg // L

@@ -4,16 +4,16 @@ grid before it runs on a GPU: every load of A, SFA, B and SFB is inside its
 buffer, every (row, chunk) of A is taken by exactly one live lane slot, every
 output (vector, row) is written exactly once, and nothing outside c is. Keep in
 step with the kernel: 4 waves of 64 lanes, 2 tiles of 16 rows per workgroup,
-the whole steps of 4 chunks split contiguously between the waves (scale pairs
-addressed as chunk g's pair plus s steps), a ragged last step taken by the last
-wave, lane group g = lane/16 on chunk g of a step, the 16x16 result with lane L holding rows 4 (L/16) + j
+the whole steps of 4 chunks dealt to the waves in turn, GROUP consecutive
+steps at a time (scale pairs addressed as chunk g's pair plus s steps), a
+ragged last step taken by the last wave, lane group g = lane/16 on chunk g of a step, the 16x16 result with lane L holding rows 4 (L/16) + j
 of vector slot L % 16."""
 import numpy as np
 import pytest
 
 import block_scaled_fp4_gemv_amd as g
 
-WAVES, RT = 4, 2
+WAVES, RT, GROUP = 4, 2, 2
 
 
 def pair_offset(r, c, nkb, ncb, layout):
@@ -22,8 +22,18 @@ def pair_offset(r, c, nkb, ncb, layout):
     return ((r >> 7) * ncb + (c >> 1)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 1) * 2
 
 
+def wave_steps(wave, nfull, group=GROUP):
+    """The K-steps of one wave, in its order: the kernel's local step u maps
+    to (u // group) * WAVES * group + wave * group + u % group."""
+    span = WAVES * group
+    ncyc = nfull // span
+    nu = ncyc * group + min(max(nfull - ncyc * span - wave * group, 0), group)
+    return [(u // group) * span + wave * group + u % group for u in range(nu)]
+
+
 def emulate(M, N, K, L, layout):
-    plan = g.nvfp4_gemm_small_n_plan(M, N, K, L)
+    plan = g.nvfp4_gemm_small_n_plan(M, N, K, L, layout)
+    assert plan["lds_bytes"] == 0, "the unstaged kernel runs for this shape and layout"
     P = -(-M // (16 * RT))
     assert plan["workgroups"] == L * P
     nchunks, nkb = K // 32, K // 16
@@ -64,8 +74,8 @@ def emulate(M, N, K, L, layout):
             assert sb.min() >= 0 and (sb + 2).max() <= L * sfb_batch
 
         for wave in range(WAVES):
-            s_begin, s_end = wave * nfull // WAVES, (wave + 1) * nfull // WAVES
-            for s in range(s_begin, s_end):
+            for s in wave_steps(wave, nfull):
+                assert 0 <= s < nfull
                 visit(s, 4 * s + grp, np.ones(64, bool), True)
         if nchunks % 4:          # the ragged last step, taken by the last wave
             c = np.minimum(4 * nfull + grp, nchunks - 1)
@@ -78,11 +88,26 @@ def emulate(M, N, K, L, layout):
     return taken, written
 
 
-@pytest.mark.parametrize("M,N,K,L", [(1, 3, 32, 1), (7, 3, 96, 2), (33, 8, 160, 1), (64, 4, 4096, 1),
-                                     (129, 5, 1056, 2), (300, 4, 20480, 1), (45, 7, 224, 3),
-                                     (100, 5, 160, 300), (300, 4, 1056, 120)])
-@pytest.mark.parametrize("layout", ["plain", "blocked"])
+@pytest.mark.parametrize("M,N,K,L,layout", [
+    (M, N, K, L, "plain") for M, N, K, L in [(1, 3, 32, 1), (7, 3, 96, 2), (33, 8, 160, 1), (64, 4, 4096, 1),
+                                             (129, 5, 1056, 2), (300, 4, 20480, 1), (45, 7, 224, 3),
+                                             (100, 5, 160, 300), (300, 4, 1056, 120)]] + [
+    # blocked scales take this kernel past K = 16384 only
+    (M, N, K, L, "blocked") for M, N, K, L in [(300, 4, 20480, 1), (33, 8, 16416, 2), (129, 3, 32768, 1)]])
 def test_mfma_kernel_indexing(M, N, K, L, layout):
     taken, written = emulate(M, N, K, L, layout)
     assert np.all(taken == 1), "each (row, chunk) of A is taken exactly once"
     assert np.all(written == 1), "each output is written exactly once"
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_wave_steps_partition(group):
+    """The waves' steps are a partition of 0 .. nfull-1, each wave's in
+    increasing order, for every step count up to a few spans."""
+    for nfull in range(0, 5 * WAVES * group + 3):
+        seen = []
+        for wave in range(WAVES):
+            st = wave_steps(wave, nfull, group)
+            assert st == sorted(st)
+            seen += st
+        assert sorted(seen) == list(range(nfull))

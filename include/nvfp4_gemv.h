@@ -245,7 +245,8 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
 /* Launch plan of nvfp4_gemm_small_n's own kernels for a shape and scale
  * layout: rows per workgroup, workgroups (256 threads each) and dynamic LDS
  * bytes. From N = 3 the workgroups own 32 rows; with blocked scales, where B,
- * the SFB pairs and a workgroup's SFA lines fit in LDS (K <= 16384), they are
+ * the SFB lines and a workgroup's SFA lines fit in LDS (about (3N/4 + 2) * K
+ * bytes within 150 KiB: K up to 16384 for N = 8, 32768 for N = 3), they are
  * staged there (lds_bytes > 0) and each 128-row block has 4 workgroups. Any
  * output pointer may be NULL. Returns NVFP4_ERR_INVALID_SHAPE for shapes it
  * does not take, NVFP4_ERR_INVALID_LAYOUT for an unknown layout. */

@@ -300,14 +300,16 @@ def test_small_n_plan():
     assert p["workgroups"] == 2 and p["rows_per_wg"] == 7
     # blocked scales: the staged kernel, 4 workgroups per 128-row block, B and the scales in LDS
     p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1, "blocked")
-    assert p["workgroups"] == 224 and p["rows_per_wg"] == 32 and 0 < p["lds_bytes"] <= 150 * 1024
+    assert p["workgroups"] == 224 and p["rows_per_wg"] == 32 and 0 < p["lds_bytes"] <= 96 * 1024
     p = g.nvfp4_gemm_small_n_plan(7, 3, 96, 2, "blocked")
     assert p["workgroups"] == 8 and p["rows_per_wg"] == 7 and p["lds_bytes"] > 0
     p = g.nvfp4_gemm_small_n_plan(1000, 4, 4096, 3, "blocked")
     assert p["workgroups"] == 3 * 8 * 4
-    # past K = 16384 the blocked scales take the unstaged kernel
-    p = g.nvfp4_gemm_small_n_plan(300, 4, 20480, 1, "blocked")
-    assert p["workgroups"] == 10 and p["lds_bytes"] == 0
+    # the staged kernel's LDS does not depend on K: three slots of one block of 32 K-steps
+    p = g.nvfp4_gemm_small_n_plan(300, 4, 40960, 1, "blocked")
+    assert p["workgroups"] == 12 and p["lds_bytes"] == 3 * 32 * (64 * 4 + 256 + 8 * 4)
+    p = g.nvfp4_gemm_small_n_plan(300, 5, 40960, 1, "blocked")
+    assert p["lds_bytes"] == 3 * 32 * (64 * 8 + 256 + 8 * 8)
     with pytest.raises(g.Nvfp4Error):
         g.nvfp4_gemm_small_n_plan(128, 9, 256, 1)
     with pytest.raises(g.Nvfp4Error):

@@ -1,51 +1,34 @@
 """CPU mirror of the staged matrix-core N-vector kernel's index arithmetic
 (nvfp4_gemm_small_n_mfma_staged_kernel in nvfp4_gemm_small_n.hip), run over its
-whole grid before it runs on a GPU. For every workgroup it replays the
-prologue's copies into a model of LDS (which global byte each LDS byte holds),
-then every LDS read and global load of the loop and the ragged last step, and
-checks: global loads inside their buffers, LDS copies and reads inside the
-dynamic LDS and each region, every LDS read returning exactly the scale pair or
-chunk of B the MFMA step needs, every (row, chunk) of A taken exactly once, and
-every output written exactly once.
+whole grid before it runs on a GPU. Block by block it replays the staging
+wave's copies into a model of the block's LDS slot (which global byte each LDS
+byte holds), then every LDS read the computing waves make in that block and
+every global load of A (the first ring, the refills, the ragged last step),
+and checks: loads inside their buffers,
+copies and reads inside the slot, every LDS read returning exactly the scale
+pair or chunk of B its MFMA step needs, every (row, chunk) of A taken exactly
+once, every output written exactly once.
 
-Keep in step with the kernel: 4 waves of 64 lanes, 2 tiles of 16 rows;
-workgroup h of a 128-row block owns rows 8h + p + 32j (p < 8, j < 4); MFMA row m
-of tile t is row 8h + (m & 7) + 32 (2 (m >> 3) + t); wave w takes the K-steps
-w, w + 4, ...; lane group g = lane / 16 takes chunk 4s + g of step s; the LDS
-layout of ms_layout; the ragged last step by the last wave."""
+Keep in step with the kernel: wave 0 stages, waves 1..4 compute (cw = 0..3), 2
+tiles of 16 rows; workgroup h of a 128-row block owns rows 8h + p + 32j (p < 8,
+j < 4); MFMA row m of tile t is row 8h + (m & 7) + 32 (2 (m >> 3) + t);
+computing wave cw takes the K-steps 4u + cw; block k is the K-steps 32k ..
+32k+31 in slot k % 3 (each block is modelled in a fresh slot: the staging
+wave's order is checked by the barrier count); lane group g = lane / 16 takes
+chunk 4s + g of step s; copies whose K-steps all lie past the last are skipped;
+the slot layout of MsSlot; the ragged last step by the last computing wave."""
 import numpy as np
 import pytest
 
 import block_scaled_fp4_gemv_amd as g
 
-WAVES, RT, THREADS, MAXN = 4, 2, 256, 8
-DMA = 64 * 16
-LDS_LIMIT = 150 * 1024
-MAX_DMA_PER_WAVE = 40
+CWAVES, RT, BLK, LOCAL, RING = 4, 2, 32, 8, 4
 
 
-def layout(K, N):
-    nchunks, ncb = K // 32, (K // 16 + 3) // 4
-    n_dma_b = (nchunks + 63) // 64
-    n_dma_sfa = (ncb * 8 + 63) // 64
-    b_vec = n_dma_b * DMA + 16
-    sfb_vec = (ncb * 4 + 127) // 128 * 128 + 8
-    return dict(n_dma_b=n_dma_b, n_dma_sfa=n_dma_sfa, b_vec=b_vec, sfb_vec=sfb_vec,
-                b_bytes=(N * b_vec + 127) // 128 * 128, sfa_bytes=n_dma_sfa * DMA, sfb_bytes=N * sfb_vec)
-
-
-def staged_lds_bytes(M, N, K, L):
-    """Mirror of ms_lds_bytes: the dynamic LDS of the staged kernel, or -1."""
-    if N < 3 or N > MAXN:
-        return -1
-    o = layout(K, N)
-    total = o["b_bytes"] + o["sfa_bytes"] + o["sfb_bytes"]
-    ncb = (K // 16 + 3) // 4
-    per_wave = N * (-(-o["n_dma_b"] // WAVES)) + (-(-o["n_dma_sfa"] // WAVES))
-    if total > LDS_LIMIT or per_wave > MAX_DMA_PER_WAVE or ncb > THREADS or \
-            L * (-(-M // 128)) * 4 > 2 ** 31 - 1:
-        return -1
-    return total
+def slot_layout(N):
+    NP = 4 if N <= 4 else 8
+    kB, kSfa, kSfb = BLK * 64 * NP, BLK * 256, BLK * 8 * NP
+    return NP, kB, kSfa, kSfb
 
 
 def blocked_offset(r, kb, ncb):
@@ -53,112 +36,134 @@ def blocked_offset(r, kb, ncb):
 
 
 def emulate(M, N, K, L):
-    lds_total = staged_lds_bytes(M, N, K, L)
-    assert lds_total >= 0
     plan = g.nvfp4_gemm_small_n_plan(M, N, K, L, "blocked")
-    assert plan["lds_bytes"] == lds_total and plan["workgroups"] == L * (-(-M // 128)) * 4
-    o = layout(K, N)
+    NP, kB, kSfa, kSfb = slot_layout(N)
+    slot_bytes = kB + kSfa + kSfb
+    assert plan["lds_bytes"] == 3 * slot_bytes
+    P = -(-M // 128) * 4
+    assert plan["workgroups"] == L * P
     nchunks, nkb = K // 32, K // 16
     ncb = (nkb + 3) // 4
     nfull = nchunks // 4
+    nblk = -(-nfull // BLK)
     row_bytes = K // 2
     a_bytes, b_bytes = L * M * row_bytes, L * N * row_bytes
     sfa_batch, sfb_batch = -(-M // 128) * ncb * 512, ncb * 512
-    P = -(-M // 128) * 4
-    sB, sSFA = 0, o["b_bytes"]
-    sSFB = sSFA + o["sfa_bytes"]
     taken = np.zeros((L, M, nchunks), np.int64)
     written = np.zeros((L, N, M), np.int64)
     lane = np.arange(64)
     grp, i16 = lane >> 4, lane & 15
+    B0, SA0, SB0 = 0, 1 << 40, 2 << 40        # tags of the three global buffers
+    n = np.minimum(i16, N - 1)
+    n_live = i16 < N
+    nus = [nfull // CWAVES + (1 if cw < nfull % CWAVES else 0) for cw in range(CWAVES)]
     for lid in range(L * P):
         wgb, l = lid % P, lid // P
         blk, h = wgb // 4, wgb % 4
         rbase = blk * 128 + 8 * h
-        lds = np.full(lds_total, -1, np.int64)     # global byte index held (B: b_base +, SFA: sfa_base +, SFB: sfb_base +)
-        B0, SA0, SB0 = 0, 1 << 40, 2 << 40         # tags of the three global buffers
-
-        def store(dst, src):
-            if dst.size:
-                assert dst.min() >= 0 and dst.max() < lds_total
-                lds[dst] = src
-
-        for wave in range(WAVES):
-            for nv in range(N):                    # B copies of vector nv
-                for i in range(wave, o["n_dma_b"], WAVES):
-                    c = np.minimum(i * 64 + lane, nchunks - 1)
-                    src = (l * N + nv) * row_bytes + c * 16
-                    assert src.min() >= 0 and (src + 16).max() <= b_bytes
-                    dst = sB + nv * o["b_vec"] + i * DMA + lane * 16
-                    assert (dst + 16).max() <= sB + o["b_bytes"]
-                    for k in range(16):
-                        store(dst + k, B0 + src + k)
-            for i in range(wave, o["n_dma_sfa"], WAVES):
-                it = np.minimum(i * 64 + lane, ncb * 8 - 1)
-                src = l * sfa_batch + (blk * ncb + (it >> 3)) * 512 + (8 * h + (it & 7)) * 16
-                assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
-                dst = sSFA + i * DMA + lane * 16
-                assert (dst + 16).max() <= sSFA + o["sfa_bytes"]
-                for k in range(16):
-                    store(dst + k, SA0 + src + k)
-            tid = wave * 64 + lane                 # SFB dwords: vector nv, group q = tid
-            qs = np.minimum(tid, ncb - 1)
-            for nv in range(MAXN):
-                src = l * sfb_batch + qs * 512 + min(nv, N - 1) * 16
-                assert src.min() >= 0 and (src + 4).max() <= L * sfb_batch
-                if nv < N:
-                    ok = tid < ncb
-                    dst = sSFB + nv * o["sfb_vec"] + tid[ok] * 4
-                    assert (dst + 4).max(initial=0) <= sSFB + o["sfb_bytes"]
-                    for k in range(4):
-                        store(dst + k, SB0 + src[ok] + k)
-
-        n = np.minimum(i16, N - 1)
-        n_live = i16 < N
 
         def rows_of(t):
             return rbase + (i16 & 7) + 32 * (2 * (i16 >> 3) + t)
 
-        def check_step(c, live, a_addr_fn):
-            # B chunk c of vector n
-            lb = sB + n * o["b_vec"] + c * 16
-            for k in range(16):
-                assert np.all(lds[lb + k] == B0 + (l * N + n) * row_bytes + c * 16 + k)
-            # SFB pair (blocks 2c, 2c+1 of vector n), where live
-            lsb = sSFB + n * o["sfb_vec"] + 2 * c
-            m = live & n_live
-            for k in range(2):
-                want = SB0 + l * sfb_batch + blocked_offset(n, 2 * c + k, ncb)
-                assert np.all(lds[lsb + k][m] == want[m])
-            # SFA: an 8-byte read, tile t's dword = bytes 4t .. 4t+3, pair at 2 (c & 1)
-            lsa = sSFA + (c >> 1) * 128 + (i16 & 7) * 16 + 8 * (i16 >> 3)
-            assert lsa.min() >= sSFA and (lsa + 8).max() <= sSFA + o["sfa_bytes"]
+        def a_load(addr):
+            assert addr.min() >= 0 and (addr + 16).max() <= a_bytes
+
+        # the first ring and the refills of every computing wave (global loads of A)
+        for cw in range(CWAVES):
+            nu = nus[cw]
+            for t in range(RT):
+                r = np.minimum(rows_of(t), M - 1)
+                row0 = (l * M + r) * row_bytes
+                for d in range(RING):
+                    a_load(row0 + grp * 16 + cw * 64 + min(d, nu - 1) * 64 * CWAVES if nu > 0 else row0)
+                for u in range(nu):
+                    if u + RING < nu:
+                        a_load(row0 + grp * 16 + cw * 64 + (u + RING) * 64 * CWAVES)
+        for k in range(nblk):
+            lds = np.full(slot_bytes, -1, np.int64)
+            s0 = k * BLK
+
+            def store(dst, src):
+                assert dst.min() >= 0 and dst.max() < slot_bytes
+                lds[dst] = src
+
+            for i in range(kB // 1024):                # B: [sb][NP][4 chunks of 16 bytes]
+                if s0 + (i * 64) // (4 * NP) >= nfull:
+                    break                              # every K-step of the copy lies past the end
+                e = 64 * i + lane
+                s = np.minimum(s0 + e // (4 * NP), nfull - 1)
+                nn = np.minimum((e >> 2) % NP, N - 1)
+                src = (l * N + nn) * row_bytes + (4 * s + (e & 3)) * 16
+                assert src.min() >= 0 and (src + 16).max() <= b_bytes
+                for b in range(16):
+                    store(i * 1024 + lane * 16 + b, B0 + src + b)
+            for i in range(kSfa // 1024):              # SFA: [sb][2 groups][8 pieces of 16 bytes]
+                if s0 + 4 * i >= nfull:
+                    break
+                e = 64 * i + lane
+                s = np.minimum(s0 + (e >> 4), nfull - 1)
+                q = 2 * s + ((e >> 3) & 1)
+                src = l * sfa_batch + (blk * ncb + q) * 512 + (8 * h + (e & 7)) * 16
+                assert src.min() >= 0 and (src + 16).max() <= L * sfa_batch
+                for b in range(16):
+                    store(kB + i * 1024 + lane * 16 + b, SA0 + src + b)
+            for i in range(kSfb // 256):               # SFB: [sb][NP][2 groups][4 bytes]
+                if s0 + (i * 64) // (2 * NP) >= nfull:
+                    break
+                e = 64 * i + lane
+                s = np.minimum(s0 + e // (2 * NP), nfull - 1)
+                nn = np.minimum((e >> 1) % NP, N - 1)
+                q = 2 * s + (e & 1)
+                src = l * sfb_batch + q * 512 + nn * 16
+                assert src.min() >= 0 and (src + 4).max() <= L * sfb_batch
+                for b in range(4):
+                    store(kB + kSfa + i * 256 + lane * 4 + b, SB0 + src + b)
+
+            def read(off, size):
+                assert off.min() >= 0 and (off + size).max() <= slot_bytes
+                return np.stack([lds[off + b] for b in range(size)], axis=1)
+
+            for cw in range(CWAVES):
+                nu = nus[cw]
+                ob = (cw * NP + n) * 64 + grp * 16
+                osfb = kB + kSfa + (cw * NP + n) * 8 + 2 * grp
+                osfa = kB + cw * 256 + (grp >> 1) * 128 + (i16 & 7) * 16 + 8 * (i16 >> 3)
+                for u in range(LOCAL * k, min(LOCAL * (k + 1), nu)):
+                    d = u % LOCAL
+                    s = 4 * u + cw
+                    c = 4 * s + grp
+                    got_b = read(ob + d * 4 * 64 * NP, 16)
+                    want_b = B0 + ((l * N + n) * row_bytes + c * 16)[:, None] + np.arange(16)
+                    assert np.array_equal(got_b, want_b)
+                    got_sb = read(osfb + d * 4 * 8 * NP, 2)
+                    for b in range(2):
+                        want = SB0 + l * sfb_batch + blocked_offset(n, 2 * c + b, ncb)
+                        assert np.array_equal(got_sb[n_live, b], want[n_live])
+                    got_sa = read(osfa + d * 4 * 256, 8)
+                    for t in range(RT):
+                        r_real = rows_of(t)
+                        for b in range(2):
+                            # the pair of chunk c sits at bytes 4t + 2 (c & 1) of the 8-byte read
+                            got = got_sa[lane, 4 * t + 2 * (c & 1) + b]
+                            want = SA0 + l * sfa_batch + blocked_offset(r_real, 2 * c + b, ncb)
+                            assert np.array_equal(got, want)
+                        ok = r_real < M
+                        np.add.at(taken, (l, r_real[ok], c[ok]), 1)
+        if nchunks % 4:                                # ragged last step, from global memory
+            c = np.minimum(4 * nfull + grp, nchunks - 1)
+            live = 4 * nfull + grp < nchunks
             for t in range(RT):
                 r_real = rows_of(t)
                 r = np.minimum(r_real, M - 1)
-                for k in range(2):
-                    got = lds[lsa + 4 * t + 2 * (c & 1) + k]
-                    # padding rows (>= M) hold the tile's padding bytes; their outputs are not written
-                    want = SA0 + l * sfa_batch + blocked_offset(r_real, 2 * c + k, ncb)
-                    assert np.all(got[live] == want[live])
-                a_off = a_addr_fn(r, t)
-                assert a_off.min() >= 0 and (a_off + 16).max() <= a_bytes
-                assert np.array_equal(a_off, (l * M + r) * row_bytes + c * 16)
+                a_load((l * M + r) * row_bytes + c * 16)
+                sa = l * sfa_batch + blocked_offset(r, 2 * c, ncb)
+                assert sa.min() >= 0 and (sa + 2).max() <= L * sfa_batch
                 ok = live & (r_real < M)
                 np.add.at(taken, (l, r_real[ok], c[ok]), 1)
-
-        for wave in range(WAVES):
-            nu = nfull // WAVES + (1 if wave < nfull % WAVES else 0)
-            for u in range(nu):
-                s = u * WAVES + wave
-                assert s < nfull
-                c = 4 * s + grp
-                check_step(c, np.ones(64, bool),
-                           lambda r, t: (l * M + r) * row_bytes + grp * 16 + wave * 64 + u * 64 * WAVES)
-        if nchunks % 4:
-            c = np.minimum(4 * nfull + grp, nchunks - 1)
-            live = 4 * nfull + grp < nchunks
-            check_step(c, live, lambda r, t: (l * M + r) * row_bytes + c * 16)
+            bo = (l * N + n) * row_bytes + c * 16
+            assert bo.min() >= 0 and (bo + 16).max() <= b_bytes
+            sb = l * sfb_batch + blocked_offset(n, 2 * c, ncb)
+            assert sb.min() >= 0 and (sb + 2).max() <= L * sfb_batch
         for e in range(RT * 64 * 4):
             t, ln, j = e >> 8, (e >> 2) & 63, e & 3
             mrow = 4 * (ln >> 4) + j
@@ -170,7 +175,8 @@ def emulate(M, N, K, L):
 
 @pytest.mark.parametrize("M,N,K,L", [(1, 3, 32, 1), (7, 3, 96, 2), (33, 8, 160, 1), (128, 4, 4096, 1),
                                      (129, 5, 1056, 2), (300, 4, 16384, 1), (45, 7, 224, 3),
-                                     (256, 8, 16384, 1), (200, 3, 2048, 4), (100, 6, 7168, 2)])
+                                     (256, 8, 16384, 1), (200, 3, 2048, 4), (100, 6, 7168, 2),
+                                     (40, 4, 4224, 1), (20, 8, 40960, 1), (64, 3, 512, 1)])
 def test_staged_kernel_indexing(M, N, K, L):
     taken, written = emulate(M, N, K, L)
     assert np.all(taken == 1), "each (row, chunk) of A is taken exactly once"
@@ -178,17 +184,13 @@ def test_staged_kernel_indexing(M, N, K, L):
 
 
 def test_staged_kernel_applies():
-    """Where the staged kernel runs: the headline and batched shapes with N up
-    to 8; not beyond K = 16384 (one SFB group per lane) or past the LDS limit."""
-    for N in range(3, 9):
-        assert staged_lds_bytes(7168, N, 16384, 1) > 0
-        assert staged_lds_bytes(4096, N, 7168, 8) > 0
-    assert staged_lds_bytes(7168, 8, 16384, 1) <= LDS_LIMIT
-    assert staged_lds_bytes(64, 3, 16384 + 64, 1) == -1
-    assert staged_lds_bytes(64, 2, 4096, 1) == -1
-    for M, N, K, L in [(7168, 8, 16384, 1), (4096, 4, 7168, 8), (64, 3, 16448, 1), (100, 5, 160, 300),
-                       (1, 3, 32, 1), (1000, 8, 2048, 3)]:
-        want = staged_lds_bytes(M, N, K, L)
-        got = g.nvfp4_gemm_small_n_plan(M, N, K, L, "blocked")["lds_bytes"]
-        assert got == max(want, 0), (M, N, K, L)
+    """Blocked scales with N >= 3 take this kernel for grids of up to 256
+    workgroups at any K (its LDS does not depend on K), and past 256 where all
+    of K does not fit the up-front kernel's LDS; plain scales never do."""
+    for M, N, K, L in [(7168, 8, 16384, 1), (64, 3, 65536, 1), (1, 3, 32, 1), (7168, 4, 32768, 1),
+                       (4096, 8, 65536, 8)]:
+        NP, kB, kSfa, kSfb = slot_layout(N)
+        assert g.nvfp4_gemm_small_n_plan(M, N, K, L, "blocked")["lds_bytes"] == 3 * (kB + kSfa + kSfb)
         assert g.nvfp4_gemm_small_n_plan(M, N, K, L, "plain")["lds_bytes"] == 0
+    p2 = g.nvfp4_gemm_small_n_plan(7168, 2, 16384, 1, "blocked")
+    assert p2["workgroups"] == 256          # the dot-product kernel's plan

@@ -27,7 +27,12 @@
 // before the contraction and sum_k a' b' is a plain float16 matrix product with
 // float32 accumulation. One v_mfma_f32_16x16x32_f16 takes 16 rows of A by 16
 // vector slots (N used, the others zero) over 32 k; its cost does not depend
-// on N, where the dot-product kernel's grows with it.
+// on N, where the dot-product kernel's grows with it. Three matrix-core
+// kernels share that layout: with plain scales the unstaged one (each step
+// loads its scale pairs and B from global memory); with blocked scales a
+// staged one (B and the scales in LDS, only A read from global memory in the
+// loop), streamed by a staging wave for grids of up to one workgroup per CU,
+// staged all at once up front for larger grids.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -70,7 +75,7 @@ __device__ inline int64_t sn_pair_offset(int64_t r, int32_t c, int32_t nkb, int3
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// Matrix-core kernel. A wave owns kMfRT tiles of 16 rows and every
+// Unstaged matrix-core kernel. A wave owns kMfRT tiles of 16 rows and every
 // kMfWaves-th group of kMfGroup K-steps (one step = 4 chunks, 128 k), so the
 // kMfWaves waves of a workgroup read neighbouring pieces of the same rows at
 // the same time; their partial tiles are added in LDS in a fixed order. In a step, lane group g (lanes 16g .. 16g+15) takes chunk g:
@@ -253,15 +258,17 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_kernel(
     }
 }
 
-// Staged matrix-core kernel (blocked scales, N >= 3). Same MFMA layout as the
-// kernel above, but the computing waves read only A from global memory: per
-// step loads of the scale pairs and of B (a few bytes per lane, touching
-// several lines each) took about a third of the streaming time there. A fifth
-// wave stages B, the SFB dwords and the workgroup's SFA lines into LDS with
-// direct-to-LDS copies, one block of kMsBlkSteps K-steps ahead of the
-// computing waves, in two LDS slots; a barrier per block hands a slot over.
-// The computing waves' loads and waits never see the copies, so their rings
-// of A stay full across the blocks.
+// Streamed staged matrix-core kernel (blocked scales, N >= 3). Same MFMA
+// layout as the kernel above, but the computing waves read only A from
+// global memory: per step loads of the scale pairs and of B (a few bytes per
+// lane, touching several lines each) took about a third of the streaming
+// time there. A fifth wave stages B, the SFB dwords and the workgroup's SFA
+// lines into LDS with direct-to-LDS copies, in blocks of kMsBlkSteps K-steps,
+// two blocks ahead of the computing waves, in three LDS slots; a barrier per
+// block hands a slot over. The computing waves' loads and waits never see the
+// copies, so their rings of A stay full across the blocks (copies issued by
+// the computing waves themselves, which the compiler cannot count, made its
+// waits for the ring drain it at every block).
 //
 // Rows. A blocked scale tile is 128 rows x 4 blocks; its 16-byte piece p holds
 // the 4 blocks of rows p, p+32, p+64, p+96. Workgroup h (0..3) of a 128-row
@@ -1174,8 +1181,10 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
         case MfKind::Upfront:
             e = mu_launch(grid, mf_lds, a, b, sfa, sfb, c, q, (hipStream_t)stream);
             break;
-        default:
-            e = mf_launch<NVFP4_SF_PLAIN>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream);
+        default:                                                       // plain scales
+            e = sf_layout == NVFP4_SF_PLAIN
+                    ? mf_launch<NVFP4_SF_PLAIN>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream)
+                    : mf_launch<NVFP4_SF_BLOCKED>(grid, a, b, sfa, sfb, c, q, (hipStream_t)stream);
             break;
         }
     } else {

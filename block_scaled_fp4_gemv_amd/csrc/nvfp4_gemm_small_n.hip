@@ -1001,11 +1001,28 @@ hipError_t mf_launch(int64_t grid, const void *a, const void *b, const void *sfa
     return hipGetLastError();
 }
 
-// The staged kernel's dynamic LDS bytes (two slots), or -1 where it does
-// not run: plain scales, N < 3, or more workgroups than a grid holds.
-int64_t ms_lds_bytes(int64_t M, int64_t N, int64_t L, int sf_layout)
+// Whether a matrix-core kernel runs: from N = 3 always; N = 2 with blocked
+// scales where the staged kernels get at least kMfMinGrid2 workgroups and K is
+// at least kMfMinK2. The MFMA's cost does not depend on N: for N = 2 it ran
+// 15.6 us on the headline A and 28.8 on the batched A, against 19.0 and 38.3
+// through the two-vector GEMV kernel; with short rows (7168x2048x4: 12.2
+// against 9.8) or few workgroups the GEMV's plan uses the chip better.
+constexpr int64_t kMfMinGrid2 = 128;
+constexpr int64_t kMfMinK2 = 4096;
+bool mf_runs(int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout)
 {
-    if (sf_layout != NVFP4_SF_BLOCKED || N < kMfMinN || N > kSnMaxN ||
+    if (N >= kMfMinN)
+        return true;
+    return N == 2 && sf_layout == NVFP4_SF_BLOCKED && K >= kMfMinK2 &&
+           L * ((M + 127) / 128) * kMsWgPerBlock >= kMfMinGrid2;
+}
+
+// The streamed kernel's dynamic LDS bytes (three slots), or -1 where it does
+// not run: plain scales, no matrix-core kernel, or more workgroups than a
+// grid holds.
+int64_t ms_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout)
+{
+    if (sf_layout != NVFP4_SF_BLOCKED || !mf_runs(M, N, K, L, sf_layout) || N > kSnMaxN ||
         L * ((M + 127) / 128) * kMsWgPerBlock > INT32_MAX)
         return -1;
     return (int64_t)kMsSlots * (N <= 4 ? MsSlot<4>::kBytes : MsSlot<8>::kBytes);
@@ -1026,12 +1043,12 @@ hipError_t ms_launch(int64_t grid, int64_t lds, const void *a, const void *b, co
 }
 
 // The up-front kernel's LDS bytes for (M, N, K, L), or -1 where it does not
-// apply: N >= 3, LDS within the limit, each wave's copies within what the
+// apply: N >= 2, LDS within the limit, each wave's copies within what the
 // wait counter holds next to the ring and the SFB loads, one 4-block group of
 // SFB per lane at most (K <= 16384).
 int64_t mu_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t L)
 {
-    if (N < kMfMinN || N > kSnMaxN)
+    if (N < 2 || N > kSnMaxN)
         return -1;
     const MuLayout o = mu_layout((int32_t)K, (int32_t)N);
     const int64_t bytes = (int64_t)o.b_bytes + o.sfa_bytes + o.sfb_bytes;
@@ -1059,7 +1076,7 @@ hipError_t mu_launch(int64_t grid, int64_t lds, const void *a, const void *b, co
 enum class MfKind { Unstaged, Upfront, Streamed };
 MfKind mf_select(int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout, int64_t *lds)
 {
-    const int64_t streamed = ms_lds_bytes(M, N, L, sf_layout);
+    const int64_t streamed = ms_lds_bytes(M, N, K, L, sf_layout);
     if (streamed < 0) {
         *lds = 0;
         return MfKind::Unstaged;
@@ -1089,7 +1106,7 @@ nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t 
     if (sf_layout != NVFP4_SF_PLAIN && sf_layout != NVFP4_SF_BLOCKED)
         return NVFP4_ERR_INVALID_LAYOUT;
     int64_t mf_lds = 0;
-    if (N >= kMfMinN && mf_select(M, N, K, L, sf_layout, &mf_lds) != MfKind::Unstaged) {
+    if (mf_runs(M, N, K, L, sf_layout) && mf_select(M, N, K, L, sf_layout, &mf_lds) != MfKind::Unstaged) {
         // a staged matrix-core kernel: 4 workgroups of 32 rows per 128-row block
         if (rows_per_wg)
             *rows_per_wg = (int32_t)std::min<int64_t>(32, M);
@@ -1153,8 +1170,9 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
     // The operand layouts for N = 1 are the GEMV's.
     if (N == 1 && nvfp4_gemv_workspace_bytes(M, K, L) == 0)
         return nvfp4_gemv_scaled(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, nullptr, 0, stream);
-    // Two vectors: the GEMV kernel with b' of both in registers, where it needs no K-split.
-    if (N == 2 && nvfp4_gemv_workspace_bytes(M, K, L) == 0) {
+    // Two vectors: the GEMV kernel with b' of both in registers, where it
+    // needs no K-split and no matrix-core kernel runs.
+    if (N == 2 && !mf_runs(M, N, K, L, sf_layout) && nvfp4_gemv_workspace_bytes(M, K, L) == 0) {
         const nvfp4_status_t st2 = nvfp4_gemv_two_vectors(a, b, sfa, sfb, c, M, K, L, sf_layout, alpha, stream);
         if (st2 != NVFP4_ERR_INVALID_SHAPE)
             return st2;
@@ -1163,7 +1181,7 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
     const int64_t sfa_batch = sf_layout == NVFP4_SF_PLAIN ? M * nkb : ((M + 127) / 128) * ncb * 512;
     const int64_t sfb_batch = sf_layout == NVFP4_SF_PLAIN ? N * nkb : ((N + 127) / 128) * ncb * 512;
     hipError_t e;
-    if (N >= kMfMinN) {
+    if (mf_runs(M, N, K, L, sf_layout)) {
         MfParams q{};
         q.M = (int32_t)M;
         q.K = (int32_t)K;

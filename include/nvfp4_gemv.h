@@ -234,9 +234,10 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
  * own); no K-split and no workspace: small M*L leaves the GPU partly idle.
  * N = 1 runs the GEMV kernel (nvfp4_gemv_scaled), and N = 2 the GEMV kernel
  * with two vectors, whenever the GEMV's plan needs no split-K workspace; else
- * a dot-product kernel. From N = 3 a matrix-core kernel runs: a' = e2m1 * e4m3
- * and b' are exact in float16, so the product is a float16 MFMA with float32
- * accumulation. Either way nothing is allocated.
+ * a dot-product kernel. From N = 3 a matrix-core kernel runs (and for N = 2
+ * with blocked scales, K >= 4096 and at least 128 of its workgroups): a' =
+ * e2m1 * e4m3 and b' are exact in float16, so the product is a float16 MFMA
+ * with float32 accumulation. Either way nothing is allocated.
  */
 nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa, const void *sfb,
                                   void *c, int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout,

@@ -288,11 +288,17 @@ def test_small_n_validation():
 
 
 def test_small_n_plan():
-    # N <= 2: the dot-product kernel, one workgroup per CU
-    p = g.nvfp4_gemm_small_n_plan(7168, 2, 16384, 1)
+    # N <= 2 with plain scales: the dot-product kernel, one workgroup per CU
+    p = g.nvfp4_gemm_small_n_plan(7168, 2, 16384, 1, "plain")
     assert p["workgroups"] == 256 and p["rows_per_wg"] == 28
-    p = g.nvfp4_gemm_small_n_plan(100000, 2, 64, 1)
+    p = g.nvfp4_gemm_small_n_plan(100000, 2, 64, 1, "plain")
     assert p["lds_bytes"] <= 48 * 1024
+    # N = 2 with blocked scales: the streamed matrix-core kernel from 128 workgroups on
+    p = g.nvfp4_gemm_small_n_plan(7168, 2, 16384, 1, "blocked")
+    assert p["workgroups"] == 224 and p["lds_bytes"] == 3 * 32 * (64 * 4 + 256 + 8 * 4)
+    # below 128 workgroups N = 2 keeps the dot-product kernel's plan (R rows, N sums per wave in LDS)
+    p = g.nvfp4_gemm_small_n_plan(127, 2, 16384, 3, "blocked")
+    assert p["workgroups"] == 192 and p["lds_bytes"] == p["rows_per_wg"] * 2 * 4 * 4
     # N >= 3, plain scales: the matrix-core kernel, 32-row tiles per workgroup, static LDS only
     p = g.nvfp4_gemm_small_n_plan(7168, 8, 16384, 1, "plain")
     assert p["workgroups"] == 224 and p["rows_per_wg"] == 32 and p["lds_bytes"] == 0

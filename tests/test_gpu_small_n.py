@@ -55,7 +55,10 @@ CASES = [(1, 1, 32, 1), (7, 3, 96, 2), (128, 2, 2048, 1), (300, 4, 20480, 2), (1
          (300, 4, 1056, 120), (100, 8, 160, 300), (33, 3, 96, 5),
          # 128-row blocks whose workgroups own no row below M, a single 4-block group
          (5, 3, 768, 2), (127, 5, 2304, 3), (300, 6, 4352, 1), (1, 8, 256, 1), (129, 7, 256, 2),
-         (1000, 4, 7168, 2), (128, 4, 1280, 5), (20, 3, 64, 1), (7168, 3, 16384, 1)]
+         (1000, 4, 7168, 2), (128, 4, 1280, 5), (20, 3, 64, 1), (7168, 3, 16384, 1),
+         # N = 2 on the matrix-core kernels (blocked, K >= 4096, 128 workgroups or
+         # more): streamed, up-front; and short rows through the GEMV kernel
+         (4100, 2, 4224, 1), (2000, 2, 4224, 5), (4100, 2, 256, 1)]
 
 
 @pytest.mark.parametrize("M,N,K,L", CASES)
@@ -68,7 +71,11 @@ def test_small_n_parity(M, N, K, L):
         rep = oracle.check_report(got, ref)
         assert rep == "", f"{layout}\n{rep}"
         outs[layout] = got
-    assert np.array_equal(outs["plain"], outs["blocked"])
+    # the same kernel runs for both layouts except for N = 2 with K >= 4096 and
+    # 128 workgroups or more, where blocked scales take a matrix-core kernel and
+    # plain scales the GEMV's
+    if not (N == 2 and K >= 4096 and L * -(-M // 128) * 4 >= 128):
+        assert np.array_equal(outs["plain"], outs["blocked"])
 
 
 @pytest.mark.parametrize("N", [4, 2])
@@ -85,7 +92,8 @@ def test_small_n_alpha_and_edge_codes(N):
         assert oracle.check_report(got, ref) == ""
 
 
-@pytest.mark.parametrize("M,N,K,L", [(7168, 8, 16384, 1), (7168, 4, 16384, 1), (4096, 4, 7168, 8)])
+@pytest.mark.parametrize("M,N,K,L", [(7168, 8, 16384, 1), (7168, 4, 16384, 1), (4096, 4, 7168, 8),
+                                     (7168, 2, 16384, 1)])
 def test_small_n_headline_shape(M, N, K, L):
     """The bench's shapes (N = 4 and 8 on the headline A, the batched A): sampled
     rows of the first and last vector against the oracle."""

@@ -73,4 +73,6 @@ def check(M, N, K, L, layout):
                                      (129, 2, 16384, 1), (100000, 2, 64, 1)])
 @pytest.mark.parametrize("layout", [0, 1])
 def test_small_n_addresses(M, N, K, L, layout):
+    if layout == 1 and N == 2 and K >= 4096 and L * cdiv(M, 128) * 4 >= 128:
+        pytest.skip("blocked scales, N = 2, K >= 4096, 128 workgroups or more: a matrix-core kernel runs")
     check(M, N, K, L, layout)

@@ -176,7 +176,9 @@ def emulate(M, N, K, L):
 @pytest.mark.parametrize("M,N,K,L", [(1, 3, 32, 1), (7, 3, 96, 2), (33, 8, 160, 1), (128, 4, 4096, 1),
                                      (129, 5, 1056, 2), (300, 4, 16384, 1), (45, 7, 224, 3),
                                      (256, 8, 16384, 1), (200, 3, 2048, 4), (100, 6, 7168, 2),
-                                     (40, 4, 4224, 1), (20, 8, 40960, 1), (64, 3, 512, 1)])
+                                     (40, 4, 4224, 1), (20, 8, 40960, 1), (64, 3, 512, 1),
+                                     # N = 2 (blocked, K >= 4096, 128 workgroups or more)
+                                     (4100, 2, 4224, 1), (2000, 2, 4224, 2)])
 def test_staged_kernel_indexing(M, N, K, L):
     taken, written = emulate(M, N, K, L)
     assert np.all(taken == 1), "each (row, chunk) of A is taken exactly once"
@@ -193,4 +195,6 @@ def test_staged_kernel_applies():
         assert g.nvfp4_gemm_small_n_plan(M, N, K, L, "blocked")["lds_bytes"] == 3 * (kB + kSfa + kSfb)
         assert g.nvfp4_gemm_small_n_plan(M, N, K, L, "plain")["lds_bytes"] == 0
     p2 = g.nvfp4_gemm_small_n_plan(7168, 2, 16384, 1, "blocked")
-    assert p2["workgroups"] == 256          # the dot-product kernel's plan
+    assert p2["workgroups"] == 224 and p2["lds_bytes"] == 3 * sum(slot_layout(2)[1:])
+    p2 = g.nvfp4_gemm_small_n_plan(127, 2, 16384, 3, "blocked")
+    assert p2["workgroups"] == 192          # below 128 workgroups: the dot-product kernel's plan

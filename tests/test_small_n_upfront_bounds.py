@@ -36,7 +36,7 @@ def layout(K, N):
 
 def staged_lds_bytes(M, N, K, L):
     """Mirror of mu_lds_bytes: the dynamic LDS of the up-front kernel, or -1."""
-    if N < 3 or N > MAXN:
+    if N < 2 or N > MAXN:
         return -1
     o = layout(K, N)
     total = o["b_bytes"] + o["sfa_bytes"] + o["sfb_bytes"]
@@ -174,7 +174,7 @@ def emulate(M, N, K, L):
                                      (129, 5, 1056, 2), (300, 4, 16384, 1), (45, 7, 224, 3),
                                      (256, 8, 16384, 1), (200, 3, 2048, 4), (100, 6, 7168, 2),
                                      # grids of more than 256 workgroups: the library runs this kernel
-                                     (8320, 3, 256, 1), (600, 5, 160, 14)])
+                                     (8320, 3, 256, 1), (600, 5, 160, 14), (8320, 2, 4096, 1)])
 def test_upfront_kernel_indexing(M, N, K, L):
     taken, written = emulate(M, N, K, L)
     assert np.all(taken == 1), "each (row, chunk) of A is taken exactly once"
@@ -189,15 +189,18 @@ def streamed_lds_bytes(N):
 @pytest.mark.parametrize("M,N,K,L", [(7168, 8, 16384, 1), (4096, 4, 7168, 8), (4096, 8, 7168, 8),
                                      (7168, 3, 2048, 4), (7168, 4, 32768, 1), (4096, 4, 32768, 8),
                                      (64, 3, 16448, 1), (100, 5, 160, 300), (1, 3, 32, 1), (8192, 3, 256, 1),
-                                     (8320, 3, 256, 1)])
+                                     (8320, 3, 256, 1), (4096, 2, 7168, 8), (7168, 2, 16384, 1)])
 def test_kernel_choice(M, N, K, L):
-    """Mirror of mf_select: blocked scales, N >= 3: the up-front kernel for
-    grids of more than 256 workgroups where all of K fits in LDS, else the
-    streamed kernel; plain scales: the unstaged kernel (no dynamic LDS)."""
+    """Mirror of mf_runs and mf_select: blocked scales, N >= 3 (or N = 2 from
+    128 workgroups on): the up-front kernel for grids of more than 256
+    workgroups where all of K fits in LDS, else the streamed kernel; plain
+    scales: the unstaged kernel (no dynamic LDS)."""
     p = g.nvfp4_gemm_small_n_plan(M, N, K, L, "blocked")
     grid = L * (-(-M // 128)) * 4
+    assert N >= 3 or (grid >= 128 and K >= 4096)
     assert p["workgroups"] == grid
     up = staged_lds_bytes(M, N, K, L)
     want = up if grid > 256 and up >= 0 else streamed_lds_bytes(N)
     assert p["lds_bytes"] == want
-    assert g.nvfp4_gemm_small_n_plan(M, N, K, L, "plain")["lds_bytes"] == 0
+    if N >= 3:
+        assert g.nvfp4_gemm_small_n_plan(M, N, K, L, "plain")["lds_bytes"] == 0

@@ -92,6 +92,8 @@ constexpr int kRowThreads = 256;          // row kernel: 4 waves, one row each
 constexpr int kRowMaxCpl = 2;             // row kernel: chunks per lane, so K <= 64 * 2 * 32 = 4096
 constexpr int64_t kRowMaxSlots = 256;     // row kernel when the slots of all batches fit one per CU,
 constexpr int64_t kRowMaxSlotsShortK = 1024; // or four per CU with K <= 256
+constexpr int kWideMaxCpl = 4;            // wide-row kernel: K <= 256 * 4 * 32 = 32768
+constexpr int64_t kWideMaxRows = 400;     // wide-row kernel for at most this many rows (all batches)
 
 static_assert(kPrefetch % kCpl == 0, "a row's chunk-steps must not straddle the prefetch ring");
 static_assert(kDeferRounds % (kPrefetch / kCpl) == 0, "deferred rounds end on a ring boundary");
@@ -779,6 +781,72 @@ __global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_row_kernel(
         C[(int64_t)l * p.c_batch + r] = f16_bits(v * p.alpha);
 }
 
+// Wide-row kernel: the row kernel for longer rows. A workgroup of 4 waves
+// owns one row; lane j of the workgroup (wave*64 + lane) takes the chunks
+// j, j+256, ... (CPL of them, K <= 256*CPL*32), loads them with their scales
+// and B in one round, forms the scaled partial sum, and the four waves' sums
+// (DPP in each wave) are added in wave order through LDS. (Taking chunk
+// pairs with one 4-byte scale load per pair measured the same.)
+template <int LAYOUT, int CPL>
+__global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_wide_row_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
+    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, Params p)
+{
+    __shared__ float wsum[kRowThreads / 64];
+    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int32_t r = (int32_t)(lid % (uint32_t)p.M), l = (int32_t)(lid / (uint32_t)p.M);
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int32_t lane = (int32_t)threadIdx.x & 63, j = (int32_t)threadIdx.x;
+    const int32_t nchunks = p.K >> 5, nkb = p.K >> 4, ncb = (nkb + 3) >> 2;
+    const uint8_t *a_r = A + (int64_t)l * p.a_batch + (int64_t)r * p.a_row;
+    const uint8_t *b_l = B + (int64_t)l * p.b_batch;
+    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
+    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+    int32_t cc[CPL];
+    bool live[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int32_t c = j + kRowThreads * i;
+        live[i] = c < nchunks;
+        cc[i] = min(c, nchunks - 1);                                    // clamped: every load is real
+    }
+    uint4_t bq[CPL], aq[CPL];
+    uint32_t sb[CPL], sa[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        bq[i] = *(const uint4_t *)(b_l + (int64_t)cc[i] * 16);
+        sb[i] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, cc[i], nkb, ncb));
+        sa[i] = LAYOUT == NVFP4_SF_PLAIN ? *(const uint16_t *)(sfa_l + (int64_t)r * p.sfa_row + 2 * cc[i])
+                                         : *(const uint16_t *)(sfa_l + sf_pair_offset<LAYOUT>(r, cc[i], nkb, ncb));
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        aq[i] = __builtin_nontemporal_load((const uint4_t *)(a_r + (int64_t)cc[i] * 16));
+    __builtin_amdgcn_sched_barrier(0);                                  // one round of loads (see the row kernel)
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        uint4_t bp[4];
+        make_bprime(bq[i], sb[i], bp);
+        const float lo = dot_block(aq[i].x, aq[i].y, bp[0], bp[1]);
+        const float hi = dot_block(aq[i].z, aq[i].w, bp[2], bp[3]);
+        const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sa[i], false);
+        const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc));
+        acc = live[i] ? nacc : acc;
+    }
+    const float v = group_sum<64>(acc);
+    if (lane == 63)
+        wsum[wave] = v;
+    __syncthreads();
+    if (j == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kRowThreads / 64; ++w)
+            t += wsum[w];
+        C[(int64_t)l * p.c_batch + r] = f16_bits(t * p.alpha);
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 struct Plan {
@@ -794,6 +862,7 @@ struct Plan {
     int ilv;              // deferred rounds finished one per following round
     int nv;               // right-hand vectors (1 for the GEMV)
     int row_cpl;          // > 0: the row kernel with this many chunks per lane
+    int wide_cpl;         // > 0: the wide-row kernel with this many chunks per lane
     int64_t n_wg;
     int lds_bytes;
     size_t ws_partials;   // bytes of float32 partials (after the ticket region)
@@ -943,6 +1012,22 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
         pl.bfirst = pl.ilv = 0;
         return pl;
     }
+    if (nv == 1 && S == 1 && nchunks > 64 * kRowMaxCpl && nchunks <= kRowThreads * kWideMaxCpl &&
+        (int64_t)L * M <= kWideMaxRows) {
+        // few rows, longer K: one row per workgroup of 4 waves, one round of
+        // loads (wide-row kernel). Measured against the main kernel:
+        // 127x16384x1 4.26 -> 3.12-3.33 us, 127x16384x3 4.67 -> 4.34-4.41;
+        // with 896 or 1000 rows it was slower (4.9 -> 6.7 us), hence the bound.
+        pl.wide_cpl = pow2_ceil(cdiv(nchunks, kRowThreads));
+        pl.spw = 1;
+        pl.P = M;
+        pl.n_wg = (int64_t)L * M;
+        pl.lpr = kRowThreads;
+        pl.stage_bytes = 0;
+        pl.lds_bytes = 0;
+        pl.bfirst = pl.ilv = 0;
+        return pl;
+    }
     pl.stage_bytes = stage_bytes(pl.lpr, spw);
     pl.lds_bytes = (int)lds_of(spw);
     pl.wide_plain = (nchunks % 8 == 0 && kc % 8 == 0) ? 1 : 0;
@@ -1025,6 +1110,23 @@ hipError_t launch_row(const Plan &pl, const void *a, const void *b, const void *
     case 2: return go(nvfp4_gemv_row_kernel<LAYOUT, 2>);
     case 4: return go(nvfp4_gemv_row_kernel<LAYOUT, 4>);
     default: return go(nvfp4_gemv_row_kernel<LAYOUT, 8>);
+    }
+}
+
+template <int LAYOUT>
+hipError_t launch_wide_row(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
+                           void *c, const Params &p, hipStream_t st)
+{
+    const dim3 grid((uint32_t)pl.n_wg), block(kRowThreads);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
+                           (const uint8_t *)sfb, (uint16_t *)c, p);
+        return hipGetLastError();
+    };
+    switch (pl.wide_cpl) {
+    case 1: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 1>);
+    case 2: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 2>);
+    default: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 4>);
     }
 }
 
@@ -1113,6 +1215,9 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
     if (pl.row_cpl > 0) {
         e = sf_layout == NVFP4_SF_PLAIN ? launch_row<NVFP4_SF_PLAIN>(pl, a, b, sfa, sfb, c, p, st)
                                         : launch_row<NVFP4_SF_BLOCKED>(pl, a, b, sfa, sfb, c, p, st);
+    } else if (pl.wide_cpl > 0) {
+        e = sf_layout == NVFP4_SF_PLAIN ? launch_wide_row<NVFP4_SF_PLAIN>(pl, a, b, sfa, sfb, c, p, st)
+                                        : launch_wide_row<NVFP4_SF_BLOCKED>(pl, a, b, sfa, sfb, c, p, st);
     } else if (pl.nv == 2) {
         // two vectors, dense: B [L][2][K/2], SFB per vector a row (plain) or
         // the next 16-byte line of each tile (blocked), C [L][2][M]
@@ -1375,11 +1480,11 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
         return st;
     const Plan pl = make_plan(M, K, L);
     plan->lanes_per_row = pl.lpr;
-    plan->rows_per_wg = 4 * pl.spw;
+    plan->rows_per_wg = pl.wide_cpl > 0 ? 1 : 4 * pl.spw;
     plan->k_splits = pl.S;
     plan->k_per_split = pl.kc_split * 32;
     plan->workgroups = pl.n_wg;
-    plan->threads_per_wg = pl.row_cpl > 0 ? kRowThreads : kBlock;
+    plan->threads_per_wg = (pl.row_cpl > 0 || pl.wide_cpl > 0) ? kRowThreads : kBlock;
     plan->lds_bytes = pl.lds_bytes;
     return NVFP4_OK;
 }

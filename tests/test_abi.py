@@ -134,9 +134,15 @@ def test_plans(w):
     assert p["k_per_split"] % 32 == 0
     assert p["k_splits"] * p["k_per_split"] >= w.K > (p["k_splits"] - 1) * p["k_per_split"]
     ns = 32 * (w.M // 128) + min(32, w.M % 128)
+    assert p["lds_bytes"] <= 159 * 1024       # a workgroup fits the CU's 160 KiB of LDS
+    nchunks = w.K // 32
+    if 128 < nchunks <= 1024 and w.M * w.L <= 400 and p["k_splits"] == 1:
+        # few rows, longer K: the wide-row kernel, one row per workgroup of 4 waves
+        assert p["threads_per_wg"] == 256 and p["rows_per_wg"] == 1 and p["lanes_per_row"] == 256
+        assert p["workgroups"] == w.M * w.L and p["lds_bytes"] == 0
+        return
     tiles = synth.ceil_div(ns, p["rows_per_wg"] // 4)
     assert p["workgroups"] == tiles * w.L * p["k_splits"]
-    assert p["lds_bytes"] <= 159 * 1024       # a workgroup fits the CU's 160 KiB of LDS
     if w.K <= 4096 and (ns * w.L <= 256 or (w.K <= 256 and ns * w.L <= 1024)):
         # few rows: the row kernel, 4 waves of one row each, one slot per workgroup, no LDS
         assert p["threads_per_wg"] == 256 and p["rows_per_wg"] == 4 and p["lds_bytes"] == 0
@@ -149,13 +155,25 @@ def test_row_kernel_boundaries():
     """The row kernel takes K <= 4096 when the slots of all batches fit one
     workgroup per CU (four per CU with K <= 256); larger shapes, longer K and
     K-splits keep the main kernel."""
-    row = lambda M, K, L: g.nvfp4_gemv_plan(M, K, L)["threads_per_wg"] == 256
+    row = lambda M, K, L: (g.nvfp4_gemv_plan(M, K, L)["threads_per_wg"] == 256
+                           and g.nvfp4_gemv_plan(M, K, L)["rows_per_wg"] == 4)
     assert row(1024, 4096, 1) and not row(1025, 4096, 1)          # 256 slots; 257
     assert row(127, 4096, 3) and row(128, 256, 2) and row(1000, 64, 3) and row(4096, 256, 1)
     assert not row(4097, 256, 1) and not row(1000, 288, 3)        # 1025 slots; K above 256 with 750
     assert not row(7168, 16384, 1) and not row(1000, 4096, 3) and not row(896, 16384, 1)
     assert not row(127, 4128, 1)                                  # K above 64 lanes x 2 chunks
     assert not row(5, 32768, 1)                                   # long K (split)
+
+
+def test_wide_row_kernel_boundaries():
+    """The wide-row kernel takes 4096 < K <= 32768 for at most 400 rows over
+    all batches, where the plan needs no K-split."""
+    wide = lambda M, K, L: g.nvfp4_gemv_plan(M, K, L)["rows_per_wg"] == 1
+    assert wide(127, 16384, 3) and wide(127, 16384, 1) and wide(400, 8192, 1) and wide(1, 16384, 1)
+    assert not wide(401, 16384, 1) and not wide(896, 16384, 1) and not wide(1000, 16384, 1)
+    assert not wide(127, 4096, 3)                                 # the row kernel
+    assert wide(33, 4128, 2)                                      # K just past the row kernel's
+    assert not wide(1, 65536, 1) and not wide(5, 32768, 2) and not wide(1, 32768, 1)   # K-splits
 
 
 def test_long_k_is_segmented_not_split():

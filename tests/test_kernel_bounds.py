@@ -125,6 +125,65 @@ def check_row_shape(M, K, L, layout, p, ws_bytes, strides=None):
     assert np.array_equal(written, expect), "some output row is written zero or several times"
 
 
+def check_wide_row_shape(M, K, L, layout, p, ws_bytes, strides=None):
+    """The wide-row kernel (few rows, longer K): a workgroup of 4 waves owns
+    one row (workgroup lid: row lid % M of batch lid // M); thread j loads
+    chunks j, j+256, ... (clamped), their B chunks, SFB pairs and SFA pairs;
+    thread 0 writes the row's output."""
+    nchunks, nkb = K // 32, K // 16
+    ncb = cdiv(nkb, 4)
+    assert p["workgroups"] == L * M and p["rows_per_wg"] == 1 and p["k_splits"] == 1
+    assert p["lds_bytes"] == 0 and ws_bytes == 0 and p["lanes_per_row"] == ROW_THREADS
+    assert 64 * 2 < nchunks <= ROW_THREADS * 4 and L * M <= 400
+    cpl = 1
+    while ROW_THREADS * cpl < nchunks:
+        cpl *= 2
+    sd = strides or g.nvfp4_gemv_dense_strides(M, K, L, layout)
+    a_row, a_bat, b_bat, c_bat = sd["a_row"], sd["a_batch"], sd["b_batch"], sd["c_batch"]
+    sfa_row, sfa_bat, sfb_bat = sd["sfa_row"], sd["sfa_batch"], sd["sfb_batch"]
+    a_bytes = (L - 1) * a_bat + (M - 1) * a_row + K // 2
+    b_size = (L - 1) * b_bat + K // 2
+    sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512
+    sfb_batch = nkb if layout == 0 else ncb * 512
+    sfa_size = (L - 1) * sfa_bat + ((M - 1) * sfa_row + nkb if layout == 0 else sfa_batch)
+    sfb_size = (L - 1) * sfb_bat + sfb_batch
+    n_wg = p["workgroups"]
+    lids = xcd_remap(np.arange(n_wg), n_wg)
+    assert np.array_equal(np.sort(lids), np.arange(n_wg)), "remap is not a bijection"
+    j = np.arange(ROW_THREADS)
+    written = np.zeros((L - 1) * c_bat + M, np.int64)
+    taken = np.zeros((L, M, nchunks), np.int64)
+    for lid in lids:
+        r, l = lid % M, lid // M
+        assert l < L
+        for i in range(cpl):
+            c = j + ROW_THREADS * i
+            live = c < nchunks
+            cc = np.minimum(c, nchunks - 1)
+            a_off = l * a_bat + r * a_row + cc * 16
+            assert a_off.min() >= 0 and (a_off + 16).max() <= a_bytes, "A read outside the tensor"
+            b_off = l * b_bat + cc * 16
+            assert b_off.min() >= 0 and (b_off + 16).max() <= b_size, "B read outside the tensor"
+            sb = l * sfb_bat + sf_offset(layout, np.zeros_like(cc), 2 * cc, nkb, ncb)
+            assert sb.min() >= 0 and (sb + 2).max() <= sfb_size and (sb % 2 == 0).all()
+            if layout == 0:
+                sa = l * sfa_bat + r * sfa_row + 2 * cc
+            else:
+                sa = l * sfa_bat + sf_offset(1, np.full_like(cc, r), 2 * cc, nkb, ncb)
+            assert sa.min() >= 0 and (sa + 2).max() <= sfa_size and (sa % 2 == 0).all()
+            for b in range(2):
+                want = l * sfa_bat + (r * sfa_row + 2 * cc + b if layout == 0
+                                      else sf_offset(1, np.full_like(cc, r), 2 * cc + b, nkb, ncb))
+                assert np.array_equal(sa + b, want), "SFA pair is not the chunk's two scales"
+            np.add.at(taken, (l, r, cc[live]), 1)
+        written[l * c_bat + r] += 1
+    assert (taken == 1).all(), "some (row, chunk) is taken zero or several times"
+    expect = np.zeros_like(written)
+    for l in range(L):
+        expect[l * c_bat + np.arange(M)] += 1
+    assert np.array_equal(written, expect), "some output row is written zero or several times"
+
+
 def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREADS, cpl=CPL,
                 prefetch=PREFETCH, max_tickets=MAX_TICKETS, strides=None):
     """Walk the whole grid of one launch. ``plan``/``workspace_bytes`` default
@@ -133,6 +192,8 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     THREADS, CPL, PREFETCH = threads, cpl, prefetch
     p = (plan or g.nvfp4_gemv_plan)(M, K, L)
     ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
+    if p["threads_per_wg"] == ROW_THREADS and p["rows_per_wg"] == 1:
+        return check_wide_row_shape(M, K, L, layout, p, ws_bytes, strides)
     if p["threads_per_wg"] == ROW_THREADS:
         return check_row_shape(M, K, L, layout, p, ws_bytes, strides)
     lpr, spw, S = p["lanes_per_row"], p["rows_per_wg"] // 4, p["k_splits"]
@@ -327,7 +388,9 @@ SHAPES = sorted({(w.M, w.K, w.L) for w in synth.ALL} |
                  (33, 8192, 1), (1000, 4096, 3), (1000, 4096, 1), (256, 2048, 2), (4, 128, 16),
                  (7168, 32768, 1), (64, 65536, 1), (300, 20480, 2), (16, 256, 256), (2, 16384, 16),
                  (1, 352, 1), (1, 384, 1), (1, 320, 1), (128, 256, 1), (300, 4128, 1),
-                 (127, 65536, 3), (121, 65536, 2), (16, 32768, 1), (1, 1 << 22, 1)})
+                 (127, 65536, 3), (121, 65536, 2), (16, 32768, 1), (1, 1 << 22, 1),
+                 # wide-row kernel: K between 4096 and 32768, at most 400 rows
+                 (127, 32768, 3), (33, 4160, 2), (100, 8256, 3), (400, 20480, 1), (33, 4128, 2)})
 
 
 @pytest.mark.parametrize("M,K,L", SHAPES)

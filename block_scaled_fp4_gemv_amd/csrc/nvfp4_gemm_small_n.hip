@@ -348,15 +348,19 @@ __device__ __attribute__((always_inline)) inline void ms_wait_vmcnt_rt(int k)
 template <int NP>
 __global__ __launch_bounds__(kMsThreads) void nvfp4_gemm_small_n_mfma_staged_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
-    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, MfParams p)
+    const uint8_t *__restrict__ SFB, uint32_t nL, int32_t M, int32_t K, int32_t N, uint16_t *__restrict__ C,
+    MfParams p)
 {
     using S = MsSlot<NP>;
     extern __shared__ __attribute__((aligned(16))) uint8_t ms_lds[];     // kMsSlots * S::kBytes
     __shared__ float4_t ms_part[kMfWaves][kMfRT][64];
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t wgb = (int32_t)(lid % (uint32_t)p.P), l = (int32_t)(lid / (uint32_t)p.P);
+    // everything the first loads and copies depend on comes from the leading
+    // (preloaded) kernel arguments: the grid and the dense batch strides are
+    // derived from them, so no kernel-argument read precedes the first load
+    const uint32_t P = (uint32_t)((M + 127) >> 7) * kMsWgPerBlock;   // workgroups per batch
+    const uint32_t lid = xcd_remap(blockIdx.x, nL * P);
+    const int32_t wgb = (int32_t)(lid % P), l = (int32_t)(lid / P);
     const int32_t blk = wgb / kMsWgPerBlock, h = wgb % kMsWgPerBlock;
-    const int32_t M = p.M, K = p.K, N = p.N;
     const int32_t nchunks = K >> 5, ncb = ((K >> 4) + 3) >> 2;
     const int32_t nfull = nchunks >> 2;                                // whole K-steps
     const int32_t nblk = (nfull + kMsBlkSteps - 1) / kMsBlkSteps;
@@ -366,8 +370,8 @@ __global__ __launch_bounds__(kMsThreads) void nvfp4_gemm_small_n_mfma_staged_ker
     const int32_t rbase = blk * 128 + 8 * h;                           // row of p' = 0, j = 0
 
     const uint8_t *b_l = B + (int64_t)l * N * row_bytes;
-    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
-    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+    const uint8_t *sfa_l = SFA + (int64_t)l * ((M + 127) >> 7) * ncb * 512;   // blocked, dense
+    const uint8_t *sfb_l = SFB + (int64_t)l * ncb * 512;                      // N <= 128: one block of rows
 
     if (wave == 0) {
         // staging wave: block k's copies into slot k % 3, two blocks ahead of
@@ -455,6 +459,12 @@ __global__ __launch_bounds__(kMsThreads) void nvfp4_gemm_small_n_mfma_staged_ker
             abuf[d][t] = *(const uint4_t *)(nu > 0 ? a_ptr[t] + (int64_t)min(d, nu - 1) * (64 * kMfWaves) : a_row[t]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // alpha, a kernel-argument read, is taken here behind the first ring (its
+    // wait overlaps the loads in flight), not in the epilogue, where its
+    // latency would add to the kernel's end
+    float alpha = p.alpha;
+    asm volatile("" : "+s"(alpha));
+    __builtin_amdgcn_sched_barrier(0);
 
     float4_t acc[kMfRT];
 #pragma unroll
@@ -592,7 +602,7 @@ __global__ __launch_bounds__(kMsThreads) void nvfp4_gemm_small_n_mfma_staged_ker
 #pragma unroll
             for (int w = 0; w < kMfWaves; ++w)
                 v += ((const float *)&ms_part[w][t][ln])[j];
-            C[((int64_t)l * N + col) * M + row] = f16_bits(v * p.alpha);
+            C[((int64_t)l * N + col) * M + row] = f16_bits(v * alpha);
         }
     }
 }
@@ -606,7 +616,7 @@ __global__ __launch_bounds__(kMsThreads) void nvfp4_gemm_small_n_mfma_staged_ker
 // round trip, and this kernel needs fewer registers and no block barriers
 // (4096x7168x8, N = 4: 29.8 against 33.5 us; N = 8: 31.1 against 38.5).
 constexpr int kMuDmaBytes = 64 * 16;          // LDS bytes one wave-wide direct-to-LDS copy fills
-constexpr int kMuMaxNcb = kMfThreads;         // 4-block groups (K / 64) the SFB staging covers: one per lane
+constexpr int kMuMaxNcb = 256;                // 4-block groups (K / 64) at most
 constexpr int kMuMaxDmaPerWave = 40;          // direct-to-LDS copies per wave (the wait counter holds 63)
 constexpr int64_t kMuLdsLimit = 150 * 1024;   // dynamic LDS; the static partial tiles take 8 KiB more
 
@@ -615,20 +625,22 @@ struct MuLayout {
     int32_t sfb_vec;                          // LDS bytes per vector of staged SFB dwords
     int32_t b_bytes, sfa_bytes, sfb_bytes;    // LDS regions, in this order
     int32_t n_dma_b, n_dma_sfa;               // wave-wide copies per vector of B, and of SFA
+    int32_t n_dma_sfb;                        // wave-wide 4-byte copies per vector of SFB
 };
 
 // LDS layout: vector n of B at n * b_vec (chunk c at +16 c; b_vec = 16 mod 128,
 // so the vectors' chunks fall in different banks), the SFA line of 4-block
 // group q at sfa + q * 128, the SFB dword (n, q) at sfb + n * sfb_vec + 4 q
-// (sfb_vec / 4 = 2 mod 32).
+// (sfb_vec / 4 = 2 mod 32; a vector's region holds its copies whole).
 __host__ __device__ inline MuLayout mu_layout(int32_t K, int32_t N)
 {
     const int32_t nchunks = K >> 5, ncb = ((K >> 4) + 3) >> 2;
     MuLayout o;
     o.n_dma_b = (nchunks + 63) / 64;
     o.n_dma_sfa = (ncb * 8 + 63) / 64;
+    o.n_dma_sfb = (ncb + 63) / 64;
     o.b_vec = o.n_dma_b * kMuDmaBytes + 16;
-    o.sfb_vec = (ncb * 4 + 127) / 128 * 128 + 8;
+    o.sfb_vec = o.n_dma_sfb * 256 + 8;
     o.b_bytes = (N * o.b_vec + 127) / 128 * 128;
     o.sfa_bytes = o.n_dma_sfa * kMuDmaBytes;
     o.sfb_bytes = N * o.sfb_vec;
@@ -637,14 +649,18 @@ __host__ __device__ inline MuLayout mu_layout(int32_t K, int32_t N)
 
 __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_upfront_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
-    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, MfParams p)
+    const uint8_t *__restrict__ SFB, uint32_t nL, int32_t M, int32_t K, int32_t N, uint16_t *__restrict__ C,
+    MfParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t mu_lds[];
     __shared__ float4_t mu_part[kMfWaves][kMfRT][64];
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t wgb = (int32_t)(lid % (uint32_t)p.P), l = (int32_t)(lid / (uint32_t)p.P);
+    // everything the first loads and copies depend on comes from the leading
+    // (preloaded) kernel arguments: the grid and the dense batch strides are
+    // derived from them, so no kernel-argument read precedes the first load
+    const uint32_t P = (uint32_t)((M + 127) >> 7) * kMsWgPerBlock;   // workgroups per batch
+    const uint32_t lid = xcd_remap(blockIdx.x, nL * P);
+    const int32_t wgb = (int32_t)(lid % P), l = (int32_t)(lid / P);
     const int32_t blk = wgb / kMsWgPerBlock, h = wgb % kMsWgPerBlock;
-    const int32_t M = p.M, K = p.K, N = p.N;
     const int32_t nchunks = K >> 5, ncb = ((K >> 4) + 3) >> 2;
     const int32_t nfull = nchunks >> 2;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -658,8 +674,8 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_upfront_ke
     const int32_t rbase = blk * 128 + 8 * h;                          // row of p' = 0, j = 0
 
     const uint8_t *b_l = B + (int64_t)l * N * row_bytes;
-    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
-    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+    const uint8_t *sfa_l = SFA + (int64_t)l * ((M + 127) >> 7) * ncb * 512;   // blocked, dense
+    const uint8_t *sfb_l = SFB + (int64_t)l * ncb * 512;                      // N <= 128: one block of rows
 
     // the wave's local steps u = 0 .. nu-1 are the K-steps u * kMfWaves + wave
     const int32_t nu = nfull / kMfWaves + (wave < nfull % kMfWaves ? 1 : 0);
@@ -693,19 +709,20 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_upfront_ke
         const int32_t it = min(i * 64 + lane, ncb * 8 - 1);           // past the end: clamped, never read
         ms_copy16(sfa_l + ((int64_t)blk * ncb + (it >> 3)) * 512 + (8 * h + (it & 7)) * 16, sSFA + i * kMuDmaBytes);
     }
-    // SFB of vector nv, 4-block group q = tid: rows nv < 8 of the first tile row
-    uint32_t sfb_v[kSnMaxN];
-    const int32_t qs = min(tid, ncb - 1);
-#pragma unroll
-    for (int nv = 0; nv < kSnMaxN; ++nv)
-        sfb_v[nv] = *(const uint32_t *)(sfb_l + (int64_t)qs * 512 + min(nv, N - 1) * 16);
+    // SFB of vector nv, 4-block group q: the dword of rows nv < 8 in the
+    // first tile row, copied with the others (no register round trip)
+    for (int32_t nv = 0; nv < N; ++nv)
+        for (int32_t i = wave; i < lay.n_dma_sfb; i += kMfWaves)
+            ms_copy4(sfb_l + (int64_t)min(i * 64 + lane, ncb - 1) * 512 + nv * 16,   // past the end: clamped
+                     sSFB + nv * lay.sfb_vec + i * 256);
+    // alpha, a kernel-argument read, is taken here behind the first loads and
+    // copies (its wait overlaps them), not in the epilogue, where its latency
+    // would add to the kernel's end
+    __builtin_amdgcn_sched_barrier(0);
+    float alpha = p.alpha;
+    asm volatile("" : "+s"(alpha));
+    __builtin_amdgcn_sched_barrier(0);
     ms_wait_vmcnt<0>();                                               // this wave's copies have landed
-    if (tid < ncb) {
-#pragma unroll
-        for (int nv = 0; nv < kSnMaxN; ++nv)
-            if (nv < N)
-                *(uint32_t *)(sSFB + nv * lay.sfb_vec + tid * 4) = sfb_v[nv];
-    }
     __syncthreads();                                                  // B, SFB and SFA are staged
 
     float4_t acc[kMfRT];
@@ -840,7 +857,7 @@ __global__ __launch_bounds__(kMfThreads) void nvfp4_gemm_small_n_mfma_upfront_ke
 #pragma unroll
             for (int w = 0; w < kMfWaves; ++w)
                 v += ((const float *)&mu_part[w][t][ln])[j];
-            C[((int64_t)l * N + col) * M + row] = f16_bits(v * p.alpha);
+            C[((int64_t)l * N + col) * M + row] = f16_bits(v * alpha);
         }
     }
 }
@@ -1034,18 +1051,17 @@ hipError_t ms_launch(int64_t grid, int64_t lds, const void *a, const void *b, co
     if (p.N <= 4)
         hipLaunchKernelGGL(nvfp4_gemm_small_n_mfma_staged_kernel<4>, dim3((uint32_t)grid), dim3(kMsThreads),
                            (uint32_t)lds, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
-                           (const uint8_t *)sfb, (uint16_t *)c, p);
+                           (const uint8_t *)sfb, (uint32_t)p.L, p.M, p.K, p.N, (uint16_t *)c, p);
     else
         hipLaunchKernelGGL(nvfp4_gemm_small_n_mfma_staged_kernel<8>, dim3((uint32_t)grid), dim3(kMsThreads),
                            (uint32_t)lds, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
-                           (const uint8_t *)sfb, (uint16_t *)c, p);
+                           (const uint8_t *)sfb, (uint32_t)p.L, p.M, p.K, p.N, (uint16_t *)c, p);
     return hipGetLastError();
 }
 
 // The up-front kernel's LDS bytes for (M, N, K, L), or -1 where it does not
 // apply: N >= 2, LDS within the limit, each wave's copies within what the
-// wait counter holds next to the ring and the SFB loads, one 4-block group of
-// SFB per lane at most (K <= 16384).
+// wait counter holds next to the ring, at most 256 4-block groups (K <= 16384).
 int64_t mu_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t L)
 {
     if (N < 2 || N > kSnMaxN)
@@ -1054,7 +1070,8 @@ int64_t mu_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t L)
     const int64_t bytes = (int64_t)o.b_bytes + o.sfa_bytes + o.sfb_bytes;
     const int64_t ncb = (K / 16 + 3) / 4;
     if (bytes > kMuLdsLimit ||
-        N * ((o.n_dma_b + kMfWaves - 1) / kMfWaves) + (o.n_dma_sfa + kMfWaves - 1) / kMfWaves > kMuMaxDmaPerWave ||
+        N * ((o.n_dma_b + kMfWaves - 1) / kMfWaves) + (o.n_dma_sfa + kMfWaves - 1) / kMfWaves +
+                N * ((o.n_dma_sfb + kMfWaves - 1) / kMfWaves) > kMuMaxDmaPerWave ||
         ncb > kMuMaxNcb || L * ((M + 127) / 128) * kMsWgPerBlock > INT32_MAX)
         return -1;
     return bytes;
@@ -1065,7 +1082,7 @@ hipError_t mu_launch(int64_t grid, int64_t lds, const void *a, const void *b, co
 {
     hipLaunchKernelGGL(nvfp4_gemm_small_n_mfma_upfront_kernel, dim3((uint32_t)grid), dim3(kMfThreads),
                        (uint32_t)lds, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
-                       (const uint8_t *)sfb, (uint16_t *)c, p);
+                       (const uint8_t *)sfb, (uint32_t)p.L, p.M, p.K, p.N, (uint16_t *)c, p);
     return hipGetLastError();
 }
 

@@ -715,48 +715,48 @@ __global__ __launch_bounds__(kBlock) void nvfp4_gemv_kernel(
     }
 }
 
-// Row kernel for small problems: one wave per row, every load of the row
-// issued at once. The main kernel's start-up (kernel-argument read, b's
-// inputs, then the staged scales, each behind a barrier) takes about three
-// memory round trips before the first result; a workgroup of a few rows pays
-// it whole. Here a workgroup of 4 waves owns one slot (the 4 rows that share
-// the blocked scale lines) and each wave one row. Lane j takes the chunks
-// j, j+64, ... (CPL of them, K <= 64*CPL*32, short K only): it loads their B chunks, SFB
-// pairs, SFA pairs and A chunks together, waits once, forms b', the exact
-// block sums and the scaled row sum as the main kernel does, and the wave's
-// lanes are summed with DPP. No LDS, no barrier, one memory round trip.
-template <int LAYOUT, int CPL>
-__global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_row_kernel(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
-    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, Params p)
-{
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t slot = (int32_t)(lid % (uint32_t)p.ns), l = (int32_t)(lid / (uint32_t)p.ns);
-    const int32_t wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int32_t lane = (int32_t)threadIdx.x & 63;
-    const int32_t r = ((slot >> 5) << 7) + (wave << 5) + (slot & 31);   // sub-row `wave` of the slot
-    if (r >= p.M)                                                       // wave-uniform; no barrier follows
-        return;
-    const int32_t nchunks = p.K >> 5, nkb = p.K >> 4, ncb = (nkb + 3) >> 2;
-    const uint8_t *a_r = A + (int64_t)l * p.a_batch + (int64_t)r * p.a_row;
-    const uint8_t *b_l = B + (int64_t)l * p.b_batch;
-    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
-    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
-    int32_t cc[CPL];
-    bool live[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int32_t c = lane + 64 * i;
-        live[i] = c < nchunks;
-        cc[i] = min(c, nchunks - 1);                                    // clamped: every load is real
+// Strides of the row kernels' operands. DENSE: derived from M and K (the
+// layouts of the header), so that every address of the first loads depends
+// only on preloaded kernel arguments; else the caller's strides from Params,
+// a kernel-argument read before the first load.
+template <int LAYOUT, bool DENSE>
+struct RowStrides {
+    int64_t a_row, a_batch, b_batch, sfa_row, sfa_batch, sfb_batch;
+    __device__ RowStrides(int32_t M, int32_t K, const Params &p)
+    {
+        if (DENSE) {
+            const int64_t nkb = K >> 4, ncb = (nkb + 3) >> 2;
+            a_row = K >> 1;
+            a_batch = (int64_t)M * (K >> 1);
+            b_batch = K >> 1;
+            sfa_row = nkb;
+            sfa_batch = LAYOUT == NVFP4_SF_BLOCKED ? (int64_t)((M + 127) >> 7) * ncb * 512 : (int64_t)M * nkb;
+            sfb_batch = LAYOUT == NVFP4_SF_BLOCKED ? ncb * 512 : nkb;
+        } else {
+            a_row = p.a_row;
+            a_batch = p.a_batch;
+            b_batch = p.b_batch;
+            sfa_row = p.sfa_row;
+            sfa_batch = p.sfa_batch;
+            sfb_batch = p.sfb_batch;
+        }
     }
+};
+
+// One round of loads for CPL chunks of row r (chunk i of the lane: cc[i]),
+// then the scaled partial sum of the lane; used by both row kernels.
+template <int LAYOUT, int CPL>
+__device__ __attribute__((always_inline)) inline float row_partial(
+    const uint8_t *a_r, const uint8_t *b_l, const uint8_t *sfa_l, const uint8_t *sfb_l, int64_t sfa_row, int32_t r,
+    const int32_t (&cc)[CPL], const bool (&live)[CPL], int32_t nkb, int32_t ncb)
+{
     uint4_t bq[CPL], aq[CPL];
     uint32_t sb[CPL], sa[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         bq[i] = *(const uint4_t *)(b_l + (int64_t)cc[i] * 16);
         sb[i] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, cc[i], nkb, ncb));
-        sa[i] = LAYOUT == NVFP4_SF_PLAIN ? *(const uint16_t *)(sfa_l + (int64_t)r * p.sfa_row + 2 * cc[i])
+        sa[i] = LAYOUT == NVFP4_SF_PLAIN ? *(const uint16_t *)(sfa_l + (int64_t)r * sfa_row + 2 * cc[i])
                                          : *(const uint16_t *)(sfa_l + sf_pair_offset<LAYOUT>(r, cc[i], nkb, ncb));
     }
 #pragma unroll
@@ -776,9 +776,53 @@ __global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_row_kernel(
         const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc));
         acc = live[i] ? nacc : acc;
     }
+    return acc;
+}
+
+// Row kernel for small problems: one wave per row, every load of the row
+// issued at once. The main kernel's start-up (kernel-argument read, b's
+// inputs, then the staged scales, each behind a barrier) takes about three
+// memory round trips before the first result; a workgroup of a few rows pays
+// it whole. Here a workgroup of 4 waves owns one slot (the 4 rows that share
+// the blocked scale lines) and each wave one row. Lane j takes the chunks
+// j, j+64, ... (CPL of them, K <= 64*CPL*32, short K only): it loads their B chunks, SFB
+// pairs, SFA pairs and A chunks together, waits once, forms b', the exact
+// block sums and the scaled row sum as the main kernel does, and the wave's
+// lanes are summed with DPP. No LDS, no barrier, one memory round trip.
+// The leading arguments (pointers, grid size, M, K, alpha, C) fill the
+// kernel-argument SGPRs that the build preloads: the first loads and the
+// final store need no kernel-argument read (with dense strides).
+template <int LAYOUT, int CPL, bool DENSE>
+__global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_row_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
+    const uint8_t *__restrict__ SFB, uint32_t n_wg, int32_t M, int32_t K, float alpha,
+    uint16_t *__restrict__ C, Params p)
+{
+    const uint32_t lid = xcd_remap(blockIdx.x, n_wg);
+    const int32_t ns = 32 * (M >> 7) + min(M & 127, 32);                 // slots per batch
+    const int32_t slot = (int32_t)(lid % (uint32_t)ns), l = (int32_t)(lid / (uint32_t)ns);
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int32_t lane = (int32_t)threadIdx.x & 63;
+    const int32_t r = ((slot >> 5) << 7) + (wave << 5) + (slot & 31);   // sub-row `wave` of the slot
+    if (r >= M)                                                         // wave-uniform; no barrier follows
+        return;
+    const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
+    const RowStrides<LAYOUT, DENSE> sd(M, K, p);
+    const int64_t c_batch = DENSE ? (int64_t)M : p.c_batch;
+    int32_t cc[CPL];
+    bool live[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int32_t c = lane + 64 * i;
+        live[i] = c < nchunks;
+        cc[i] = min(c, nchunks - 1);                                    // clamped: every load is real
+    }
+    const float acc = row_partial<LAYOUT, CPL>(A + (int64_t)l * sd.a_batch + (int64_t)r * sd.a_row,
+                                               B + (int64_t)l * sd.b_batch, SFA + (int64_t)l * sd.sfa_batch,
+                                               SFB + (int64_t)l * sd.sfb_batch, sd.sfa_row, r, cc, live, nkb, ncb);
     const float v = group_sum<64>(acc);
     if (lane == 63)
-        C[(int64_t)l * p.c_batch + r] = f16_bits(v * p.alpha);
+        C[(int64_t)l * c_batch + r] = f16_bits(v * alpha);
 }
 
 // Wide-row kernel: the row kernel for longer rows. A workgroup of 4 waves
@@ -786,22 +830,22 @@ __global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_row_kernel(
 // j, j+256, ... (CPL of them, K <= 256*CPL*32), loads them with their scales
 // and B in one round, forms the scaled partial sum, and the four waves' sums
 // (DPP in each wave) are added in wave order through LDS. (Taking chunk
-// pairs with one 4-byte scale load per pair measured the same.)
-template <int LAYOUT, int CPL>
+// pairs with one 4-byte scale load per pair measured the same.) Arguments as
+// for the row kernel.
+template <int LAYOUT, int CPL, bool DENSE>
 __global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_wide_row_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
-    const uint8_t *__restrict__ SFB, uint16_t *__restrict__ C, Params p)
+    const uint8_t *__restrict__ SFB, uint32_t n_wg, int32_t M, int32_t K, float alpha,
+    uint16_t *__restrict__ C, Params p)
 {
     __shared__ float wsum[kRowThreads / 64];
-    const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int32_t r = (int32_t)(lid % (uint32_t)p.M), l = (int32_t)(lid / (uint32_t)p.M);
+    const uint32_t lid = xcd_remap(blockIdx.x, n_wg);
+    const int32_t r = (int32_t)(lid % (uint32_t)M), l = (int32_t)(lid / (uint32_t)M);
     const int32_t wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int32_t lane = (int32_t)threadIdx.x & 63, j = (int32_t)threadIdx.x;
-    const int32_t nchunks = p.K >> 5, nkb = p.K >> 4, ncb = (nkb + 3) >> 2;
-    const uint8_t *a_r = A + (int64_t)l * p.a_batch + (int64_t)r * p.a_row;
-    const uint8_t *b_l = B + (int64_t)l * p.b_batch;
-    const uint8_t *sfa_l = SFA + (int64_t)l * p.sfa_batch;
-    const uint8_t *sfb_l = SFB + (int64_t)l * p.sfb_batch;
+    const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
+    const RowStrides<LAYOUT, DENSE> sd(M, K, p);
+    const int64_t c_batch = DENSE ? (int64_t)M : p.c_batch;
     int32_t cc[CPL];
     bool live[CPL];
 #pragma unroll
@@ -810,30 +854,9 @@ __global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_wide_row_kernel(
         live[i] = c < nchunks;
         cc[i] = min(c, nchunks - 1);                                    // clamped: every load is real
     }
-    uint4_t bq[CPL], aq[CPL];
-    uint32_t sb[CPL], sa[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        bq[i] = *(const uint4_t *)(b_l + (int64_t)cc[i] * 16);
-        sb[i] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, cc[i], nkb, ncb));
-        sa[i] = LAYOUT == NVFP4_SF_PLAIN ? *(const uint16_t *)(sfa_l + (int64_t)r * p.sfa_row + 2 * cc[i])
-                                         : *(const uint16_t *)(sfa_l + sf_pair_offset<LAYOUT>(r, cc[i], nkb, ncb));
-    }
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-        aq[i] = __builtin_nontemporal_load((const uint4_t *)(a_r + (int64_t)cc[i] * 16));
-    __builtin_amdgcn_sched_barrier(0);                                  // one round of loads (see the row kernel)
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        uint4_t bp[4];
-        make_bprime(bq[i], sb[i], bp);
-        const float lo = dot_block(aq[i].x, aq[i].y, bp[0], bp[1]);
-        const float hi = dot_block(aq[i].z, aq[i].w, bp[2], bp[3]);
-        const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sa[i], false);
-        const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc));
-        acc = live[i] ? nacc : acc;
-    }
+    const float acc = row_partial<LAYOUT, CPL>(A + (int64_t)l * sd.a_batch + (int64_t)r * sd.a_row,
+                                               B + (int64_t)l * sd.b_batch, SFA + (int64_t)l * sd.sfa_batch,
+                                               SFB + (int64_t)l * sd.sfb_batch, sd.sfa_row, r, cc, live, nkb, ncb);
     const float v = group_sum<64>(acc);
     if (lane == 63)
         wsum[wave] = v;
@@ -843,7 +866,7 @@ __global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_wide_row_kernel(
 #pragma unroll
         for (int w = 0; w < kRowThreads / 64; ++w)
             t += wsum[w];
-        C[(int64_t)l * p.c_batch + r] = f16_bits(t * p.alpha);
+        C[(int64_t)l * c_batch + r] = f16_bits(t * alpha);
     }
 }
 
@@ -1095,39 +1118,51 @@ hipError_t launch_layout(const Plan &pl, const void *a, const void *b, const voi
     }
 }
 
-template <int LAYOUT>
-hipError_t launch_row(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb, void *c,
-                      const Params &p, hipStream_t st)
+// Dense strides: the layouts of the header (batch strides do not matter for one batch)
+bool dense_row_strides(const Params &p, int sf_layout)
+{
+    const int64_t M = p.M, K = p.K, nkb = K / 16, ncb = (nkb + 3) / 4;
+    const bool blocked = sf_layout == NVFP4_SF_BLOCKED;
+    if (p.a_row != K / 2 || (!blocked && p.sfa_row != nkb))
+        return false;
+    if (p.L == 1)
+        return true;
+    return p.a_batch == M * (K / 2) && p.b_batch == K / 2 && p.c_batch == M &&
+           p.sfa_batch == (blocked ? cdiv(M, 128) * ncb * 512 : M * nkb) &&
+           p.sfb_batch == (blocked ? ncb * 512 : nkb);
+}
+
+template <int LAYOUT, bool DENSE>
+hipError_t launch_row_kernels(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
+                              void *c, const Params &p, hipStream_t st)
 {
     const dim3 grid((uint32_t)pl.n_wg), block(kRowThreads);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
-                           (const uint8_t *)sfb, (uint16_t *)c, p);
+                           (const uint8_t *)sfb, (uint32_t)pl.n_wg, p.M, p.K, p.alpha, (uint16_t *)c, p);
         return hipGetLastError();
     };
-    switch (pl.row_cpl) {
-    case 1: return go(nvfp4_gemv_row_kernel<LAYOUT, 1>);
-    case 2: return go(nvfp4_gemv_row_kernel<LAYOUT, 2>);
-    case 4: return go(nvfp4_gemv_row_kernel<LAYOUT, 4>);
-    default: return go(nvfp4_gemv_row_kernel<LAYOUT, 8>);
+    if (pl.row_cpl > 0) {
+        switch (pl.row_cpl) {
+        case 1: return go(nvfp4_gemv_row_kernel<LAYOUT, 1, DENSE>);
+        case 2: return go(nvfp4_gemv_row_kernel<LAYOUT, 2, DENSE>);
+        case 4: return go(nvfp4_gemv_row_kernel<LAYOUT, 4, DENSE>);
+        default: return go(nvfp4_gemv_row_kernel<LAYOUT, 8, DENSE>);
+        }
+    }
+    switch (pl.wide_cpl) {
+    case 1: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 1, DENSE>);
+    case 2: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 2, DENSE>);
+    default: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 4, DENSE>);
     }
 }
 
 template <int LAYOUT>
-hipError_t launch_wide_row(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb,
-                           void *c, const Params &p, hipStream_t st)
+hipError_t launch_row(const Plan &pl, const void *a, const void *b, const void *sfa, const void *sfb, void *c,
+                      const Params &p, hipStream_t st)
 {
-    const dim3 grid((uint32_t)pl.n_wg), block(kRowThreads);
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, block, 0, st, (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa,
-                           (const uint8_t *)sfb, (uint16_t *)c, p);
-        return hipGetLastError();
-    };
-    switch (pl.wide_cpl) {
-    case 1: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 1>);
-    case 2: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 2>);
-    default: return go(nvfp4_gemv_wide_row_kernel<LAYOUT, 4>);
-    }
+    return dense_row_strides(p, LAYOUT) ? launch_row_kernels<LAYOUT, true>(pl, a, b, sfa, sfb, c, p, st)
+                                        : launch_row_kernels<LAYOUT, false>(pl, a, b, sfa, sfb, c, p, st);
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -1212,12 +1247,9 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
         p.partials = (float *)((char *)ws + kCounterBytes);
     }
     hipError_t e;
-    if (pl.row_cpl > 0) {
+    if (pl.row_cpl > 0 || pl.wide_cpl > 0) {
         e = sf_layout == NVFP4_SF_PLAIN ? launch_row<NVFP4_SF_PLAIN>(pl, a, b, sfa, sfb, c, p, st)
                                         : launch_row<NVFP4_SF_BLOCKED>(pl, a, b, sfa, sfb, c, p, st);
-    } else if (pl.wide_cpl > 0) {
-        e = sf_layout == NVFP4_SF_PLAIN ? launch_wide_row<NVFP4_SF_PLAIN>(pl, a, b, sfa, sfb, c, p, st)
-                                        : launch_wide_row<NVFP4_SF_BLOCKED>(pl, a, b, sfa, sfb, c, p, st);
     } else if (pl.nv == 2) {
         // two vectors, dense: B [L][2][K/2], SFB per vector a row (plain) or
         // the next 16-byte line of each tile (blocked), C [L][2][M]

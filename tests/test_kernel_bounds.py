@@ -414,6 +414,11 @@ STRIDED = [  # (M, K, L, layout, stride overrides)
                             sfb_batch=131072 + 1024, c_batch=200)),
     (7168, 2048, 4, 1, dict(b_batch=128 * 1024, c_batch=8192)),
     (33, 8192, 2, 0, dict(a_row=4096 + 16, sfa_row=512 + 32, sfa_batch=33 * 544, c_batch=40)),
+    # the row kernel with the caller's strides (dense strides take its preloaded-argument variant)
+    (127, 4096, 3, 1, dict(a_row=2048 + 256, a_batch=127 * 2304 + 512, b_batch=2048 + 64,
+                           sfa_batch=32768 + 512, sfb_batch=32768 + 1024, c_batch=130)),
+    (100, 2048, 2, 0, dict(a_row=1024 + 32, a_batch=100 * 1056 + 16, b_batch=1024 + 16, sfa_row=128 + 16,
+                           sfa_batch=100 * 144 + 32, sfb_batch=160, c_batch=104)),
 ]
 
 

@@ -28,9 +28,10 @@ def layout(K, N):
     nchunks, ncb = K // 32, (K // 16 + 3) // 4
     n_dma_b = (nchunks + 63) // 64
     n_dma_sfa = (ncb * 8 + 63) // 64
+    n_dma_sfb = (ncb + 63) // 64
     b_vec = n_dma_b * DMA + 16
-    sfb_vec = (ncb * 4 + 127) // 128 * 128 + 8
-    return dict(n_dma_b=n_dma_b, n_dma_sfa=n_dma_sfa, b_vec=b_vec, sfb_vec=sfb_vec,
+    sfb_vec = n_dma_sfb * 256 + 8
+    return dict(n_dma_b=n_dma_b, n_dma_sfa=n_dma_sfa, n_dma_sfb=n_dma_sfb, b_vec=b_vec, sfb_vec=sfb_vec,
                 b_bytes=(N * b_vec + 127) // 128 * 128, sfa_bytes=n_dma_sfa * DMA, sfb_bytes=N * sfb_vec)
 
 
@@ -41,8 +42,8 @@ def staged_lds_bytes(M, N, K, L):
     o = layout(K, N)
     total = o["b_bytes"] + o["sfa_bytes"] + o["sfb_bytes"]
     ncb = (K // 16 + 3) // 4
-    per_wave = N * (-(-o["n_dma_b"] // WAVES)) + (-(-o["n_dma_sfa"] // WAVES))
-    if total > LDS_LIMIT or per_wave > MAX_DMA_PER_WAVE or ncb > THREADS or \
+    per_wave = N * (-(-o["n_dma_b"] // WAVES)) + (-(-o["n_dma_sfa"] // WAVES)) + N * (-(-o["n_dma_sfb"] // WAVES))
+    if total > LDS_LIMIT or per_wave > MAX_DMA_PER_WAVE or ncb > 256 or \
             L * (-(-M // 128)) * 4 > 2 ** 31 - 1:
         return -1
     return total
@@ -103,17 +104,15 @@ def emulate(M, N, K, L):
                 assert (dst + 16).max() <= sSFA + o["sfa_bytes"]
                 for k in range(16):
                     store(dst + k, SA0 + src + k)
-            tid = wave * 64 + lane                 # SFB dwords: vector nv, group q = tid
-            qs = np.minimum(tid, ncb - 1)
-            for nv in range(MAXN):
-                src = l * sfb_batch + qs * 512 + min(nv, N - 1) * 16
-                assert src.min() >= 0 and (src + 4).max() <= L * sfb_batch
-                if nv < N:
-                    ok = tid < ncb
-                    dst = sSFB + nv * o["sfb_vec"] + tid[ok] * 4
-                    assert (dst + 4).max(initial=0) <= sSFB + o["sfb_bytes"]
+            for nv in range(N):                    # SFB dwords of vector nv: group q = i * 64 + lane
+                for i in range(wave, o["n_dma_sfb"], WAVES):
+                    q = np.minimum(i * 64 + lane, ncb - 1)
+                    src = l * sfb_batch + q * 512 + nv * 16
+                    assert src.min() >= 0 and (src + 4).max() <= L * sfb_batch
+                    dst = sSFB + nv * o["sfb_vec"] + i * 256 + lane * 4
+                    assert (dst + 4).max() <= sSFB + nv * o["sfb_vec"] + o["sfb_vec"]
                     for k in range(4):
-                        store(dst + k, SB0 + src[ok] + k)
+                        store(dst + k, SB0 + src + k)
 
         n = np.minimum(i16, N - 1)
         n_live = i16 < N

@@ -41,7 +41,9 @@ def gpu_reblock(plain, rows, K, L, offset=0):
 
 
 SHAPES = [(1, 32, 1), (1, 96, 3), (1, 16384, 1), (127, 4096, 3), (128, 2048, 2), (129, 32, 1),
-          (300, 4128, 1), (1000, 7168, 2), (7168, 2048, 4), (4096, 7168, 8), (7, 1056, 5)]
+          (300, 4128, 1), (1000, 7168, 2), (7168, 2048, 4), (4096, 7168, 8), (7, 1056, 5),
+          # 32 tiles per workgroup (ragged rows, a partial last tile group)
+          (129, 8192, 32), (100, 15872, 64), (7168, 16384, 1)]
 
 
 @pytest.mark.parametrize("rows,K,L", SHAPES)

@@ -78,7 +78,12 @@ typedef enum {
  * need, per device, grows on demand (with a device synchronisation) and keeps
  * until the process ends. Calls that overlap in time on one device therefore
  * must not use this entry point concurrently from two streams; use
- * nvfp4_gemv_ex with separate workspaces instead.
+ * nvfp4_gemv_ex with separate workspaces instead. Under HIP graph capture:
+ * make the first call of the largest split shape eagerly, before capturing
+ * (allocation is not capturable), and note that a captured graph keeps the
+ * workspace address, which a later call needing a larger workspace frees;
+ * nvfp4_gemv_ex with a caller-owned workspace, or nvfp4_gemv_noalloc, has
+ * neither concern.
  */
 nvfp4_status_t nvfp4_gemv(const void *a, const void *b, const void *sfa, const void *sfb,
                           void *c, int64_t M, int64_t K, int64_t L, int sf_layout,

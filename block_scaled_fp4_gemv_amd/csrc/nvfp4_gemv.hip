@@ -94,6 +94,9 @@ constexpr int64_t kRowMaxSlots = 256;     // row kernel when the slots of all ba
 constexpr int64_t kRowMaxSlotsShortK = 1024; // or four per CU with K <= 256
 constexpr int kWideMaxCpl = 4;            // wide-row kernel: K <= 256 * 4 * 32 = 32768
 constexpr int64_t kWideMaxRows = 400;     // wide-row kernel for at most this many rows (all batches)
+constexpr int kRowsPerWave = 8;           // multi-row kernel: rows per wave (32 per workgroup)
+constexpr int kRowsMaxCpl = 2;            // multi-row kernel: K <= 64 * 2 * 32 = 4096
+constexpr int64_t kRowsMinGrid = 192;     // multi-row kernel: grids of 192 .. 256 workgroups
 
 static_assert(kPrefetch % kCpl == 0, "a row's chunk-steps must not straddle the prefetch ring");
 static_assert(kDeferRounds % (kPrefetch / kCpl) == 0, "deferred rounds end on a ring boundary");
@@ -870,6 +873,120 @@ __global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_wide_row_kernel(
     }
 }
 
+// Multi-row kernel for short rows and many rows (K <= 4096): a workgroup of
+// 4 waves owns the 32 rows of a 128-row block whose blocked scales fill one
+// 128-byte line of every tile (rows 8h + p + 32w, p < 8: wave w takes 8 of
+// them). Lane j takes the chunks j, j+64 (CPL of them) of each of its wave's
+// rows, so b' of those chunks is formed once and used for 8 rows. Every load
+// is issued at once, one memory round trip: the blocked SFA lines by
+// direct-to-LDS copies (a line per tile, whole 1 KiB copies, ncb/8 of them),
+// B and the SFB pairs, then the 8 rows' A chunks (plain scales: each row's
+// pairs, one coalesced 128-byte run per row). Then the 8 rows' sums, each
+// reduced over its wave with DPP. Several workgroups share a CU, so each one's
+// round trip hides behind the others'. Arguments as for the row kernels.
+template <int LAYOUT, int CPL, bool DENSE>
+__global__ __launch_bounds__(kRowThreads) void nvfp4_gemv_rows_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const uint8_t *__restrict__ SFA,
+    const uint8_t *__restrict__ SFB, uint32_t n_wg, int32_t M, int32_t K, float alpha,
+    uint16_t *__restrict__ C, Params p)
+{
+    constexpr int R = kRowsPerWave;
+    extern __shared__ __attribute__((aligned(16))) uint8_t sfa_lines[];    // blocked: tile t's line at t * 128
+    const uint32_t P = (uint32_t)((M + 127) >> 7) * 4;                  // workgroups per batch
+    const uint32_t lid = xcd_remap(blockIdx.x, n_wg);
+    const int32_t l = (int32_t)(lid / P);
+    const uint32_t t = lid % P;
+    const int32_t rb = (int32_t)(t >> 2), h = (int32_t)(t & 3);
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int32_t lane = (int32_t)threadIdx.x & 63;
+    const int32_t nchunks = K >> 5, nkb = K >> 4, ncb = (nkb + 3) >> 2;
+    const RowStrides<LAYOUT, DENSE> sd(M, K, p);
+    const int64_t c_batch = DENSE ? (int64_t)M : p.c_batch;
+    const int32_t r0 = rb * 128 + 8 * h + 32 * wave;                   // row of p = 0
+    const uint8_t *a_l = A + (int64_t)l * sd.a_batch;
+    const uint8_t *b_l = B + (int64_t)l * sd.b_batch;
+    const uint8_t *sfa_l = SFA + (int64_t)l * sd.sfa_batch;
+    const uint8_t *sfb_l = SFB + (int64_t)l * sd.sfb_batch;
+
+    int32_t cc[CPL];
+    bool live[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int32_t c = lane + 64 * i;
+        live[i] = c < nchunks;
+        cc[i] = min(c, nchunks - 1);                                    // clamped: every load is real
+    }
+    // blocked: this wave's share of the line copies (copy i: tiles 8i .. 8i+7,
+    // lane -> tile 8i + lane/8, 16-byte piece lane%8; past the last tile clamped)
+    int32_t n_copies = 0;
+    if (LAYOUT == NVFP4_SF_BLOCKED) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                        // nothing in flight yet
+        const int32_t nsc = (ncb + 7) >> 3;
+        for (int32_t i = wave; i < nsc; i += kRowThreads / 64) {
+            const int32_t tile = min(8 * i + (lane >> 3), ncb - 1);
+            copy16_to_lds(sfa_l + ((int64_t)rb * ncb + tile) * 512 + h * 128 + (lane & 7) * 16,
+                          sfa_lines + i * kDmaBytes);
+            ++n_copies;
+        }
+    }
+    uint4_t bq[CPL], aq[R][CPL];
+    uint32_t sb[CPL], sa[R][CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        bq[i] = *(const uint4_t *)(b_l + (int64_t)cc[i] * 16);
+        sb[i] = *(const uint16_t *)(sfb_l + sf_pair_offset<LAYOUT>(0, cc[i], nkb, ncb));
+    }
+    if (LAYOUT == NVFP4_SF_PLAIN) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int32_t r = min(r0 + q, M - 1);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                sa[q][i] = *(const uint16_t *)(sfa_l + (int64_t)r * sd.sfa_row + 2 * cc[i]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const uint8_t *a_r = a_l + (int64_t)min(r0 + q, M - 1) * sd.a_row;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            aq[q][i] = __builtin_nontemporal_load((const uint4_t *)(a_r + (int64_t)cc[i] * 16));
+    }
+    __builtin_amdgcn_sched_barrier(0);                                  // one round of loads
+    if (LAYOUT == NVFP4_SF_BLOCKED) {
+        // the copies were issued before every other load of this wave, and
+        // loads complete in order: wait until only the later ones are left
+        wait_vmcnt(CPL * (2 + R));
+        __syncthreads();                                                // every wave's lines are staged
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                sa[q][i] = *(const uint16_t *)(sfa_lines + (cc[i] >> 1) * 128 + q * 16 + wave * 4 + (cc[i] & 1) * 2);
+    }
+    (void)n_copies;
+    uint4_t bp[CPL][4];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        make_bprime(bq[i], sb[i], bp[i]);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const float lo = dot_block(aq[q][i].x, aq[q][i].y, bp[i][0], bp[i][1]);
+            const float hi = dot_block(aq[q][i].z, aq[q][i].w, bp[i][2], bp[i][3]);
+            const float2_t sf = __builtin_amdgcn_cvt_pk_f32_fp8(sa[q][i], false);
+            const float nacc = __builtin_fmaf(hi, sf.y, __builtin_fmaf(lo, sf.x, acc));
+            acc = live[i] ? nacc : acc;
+        }
+        const float v = group_sum<64>(acc);
+        const int32_t r = r0 + q;
+        if (lane == 63 && r < M)
+            C[(int64_t)l * c_batch + r] = f16_bits(v * alpha);
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 struct Plan {
@@ -886,6 +1003,7 @@ struct Plan {
     int nv;               // right-hand vectors (1 for the GEMV)
     int row_cpl;          // > 0: the row kernel with this many chunks per lane
     int wide_cpl;         // > 0: the wide-row kernel with this many chunks per lane
+    int rows_cpl;         // > 0: the multi-row kernel with this many chunks per lane
     int64_t n_wg;
     int lds_bytes;
     size_t ws_partials;   // bytes of float32 partials (after the ticket region)
@@ -901,6 +1019,19 @@ constexpr size_t kCounterBytes = kMaxTickets * sizeof(uint32_t);
 static_assert(kTargetWGs <= kMaxTickets, "split shapes need at most kTargetWGs tickets");
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Where the multi-row kernel runs (short K, rows not taken by the row
+// kernel): when its grid is one workgroup for nearly every CU. With several
+// workgroups per CU the CUs holding one more workgroup set the time, and the
+// main kernel streams better: 7168x2048x4 8.0 -> 8.4 us, 7168x4096x3 10.4 ->
+// 11.5, 1000x4096x3 4.42 -> 4.65, 7168x64x3 3.87 -> 4.74; with one per CU,
+// 7168x64x1 3.55 -> 3.14 and 7168x4096x1 5.34 -> 5.25 (A/B, two passes).
+inline bool rows_kernel_applies(int64_t M, int64_t K, int64_t L)
+{
+    (void)K;
+    const int64_t grid = L * ((M + 127) / 128) * 4;
+    return grid >= kRowsMinGrid && grid <= kTargetWGs;
+}
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1035,6 +1166,19 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
         pl.bfirst = pl.ilv = 0;
         return pl;
     }
+    if (nv == 1 && S == 1 && nchunks <= 64 * kRowsMaxCpl && rows_kernel_applies(M, K, L)) {
+        // many rows, short K: the multi-row kernel (32 rows per workgroup,
+        // several workgroups per CU, one memory round trip each)
+        pl.rows_cpl = pow2_ceil(cdiv(nchunks, 64));
+        pl.spw = 8;
+        pl.P = (int)(cdiv(M, 128) * 4);
+        pl.n_wg = (int64_t)L * pl.P;
+        pl.lpr = 64;
+        pl.stage_bytes = 0;
+        pl.lds_bytes = (int)(cdiv(cdiv(K / 16, 4), 8) * kDmaBytes);
+        pl.bfirst = pl.ilv = 0;
+        return pl;
+    }
     if (nv == 1 && S == 1 && nchunks > 64 * kRowMaxCpl && nchunks <= kRowThreads * kWideMaxCpl &&
         (int64_t)L * M <= kWideMaxRows) {
         // few rows, longer K: one row per workgroup of 4 waves, one round of
@@ -1142,6 +1286,16 @@ hipError_t launch_row_kernels(const Plan &pl, const void *a, const void *b, cons
                            (const uint8_t *)sfb, (uint32_t)pl.n_wg, p.M, p.K, p.alpha, (uint16_t *)c, p);
         return hipGetLastError();
     };
+    if (pl.rows_cpl > 0) {
+        auto go_lds = [&](auto kern) {
+            hipLaunchKernelGGL(kern, grid, block, LAYOUT == NVFP4_SF_BLOCKED ? pl.lds_bytes : 0, st,
+                               (const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sfa, (const uint8_t *)sfb,
+                               (uint32_t)pl.n_wg, p.M, p.K, p.alpha, (uint16_t *)c, p);
+            return hipGetLastError();
+        };
+        return pl.rows_cpl == 1 ? go_lds(nvfp4_gemv_rows_kernel<LAYOUT, 1, DENSE>)
+                                : go_lds(nvfp4_gemv_rows_kernel<LAYOUT, 2, DENSE>);
+    }
     if (pl.row_cpl > 0) {
         switch (pl.row_cpl) {
         case 1: return go(nvfp4_gemv_row_kernel<LAYOUT, 1, DENSE>);
@@ -1247,7 +1401,7 @@ nvfp4_status_t launch(const void *a, const void *b, const void *sfa, const void 
         p.partials = (float *)((char *)ws + kCounterBytes);
     }
     hipError_t e;
-    if (pl.row_cpl > 0 || pl.wide_cpl > 0) {
+    if (pl.row_cpl > 0 || pl.wide_cpl > 0 || pl.rows_cpl > 0) {
         e = sf_layout == NVFP4_SF_PLAIN ? launch_row<NVFP4_SF_PLAIN>(pl, a, b, sfa, sfb, c, p, st)
                                         : launch_row<NVFP4_SF_BLOCKED>(pl, a, b, sfa, sfb, c, p, st);
     } else if (pl.nv == 2) {
@@ -1516,7 +1670,7 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
     plan->k_splits = pl.S;
     plan->k_per_split = pl.kc_split * 32;
     plan->workgroups = pl.n_wg;
-    plan->threads_per_wg = (pl.row_cpl > 0 || pl.wide_cpl > 0) ? kRowThreads : kBlock;
+    plan->threads_per_wg = (pl.row_cpl > 0 || pl.wide_cpl > 0 || pl.rows_cpl > 0) ? kRowThreads : kBlock;
     plan->lds_bytes = pl.lds_bytes;
     return NVFP4_OK;
 }

@@ -147,8 +147,25 @@ def test_plans(w):
         # few rows: the row kernel, 4 waves of one row each, one slot per workgroup, no LDS
         assert p["threads_per_wg"] == 256 and p["rows_per_wg"] == 4 and p["lds_bytes"] == 0
         assert p["lanes_per_row"] == 64
+    elif w.K <= 4096 and 192 <= w.L * synth.ceil_div(w.M, 128) * 4 <= 256:
+        # short rows, a grid of about one workgroup per CU: the multi-row
+        # kernel, 32 rows per workgroup of 4 waves, the blocked SFA lines in LDS
+        assert p["threads_per_wg"] == 256 and p["rows_per_wg"] == 32 and p["lanes_per_row"] == 64
+        assert p["lds_bytes"] == synth.ceil_div(synth.ceil_div(w.K // 16, 4), 8) * 1024
     else:
         assert p["threads_per_wg"] == 320      # 4 computing waves and the staging wave
+
+
+def test_multi_row_kernel_boundaries():
+    """The multi-row kernel takes short rows (K <= 4096, not the row kernel's)
+    where its grid of 32-row workgroups is 192 to 256 workgroups; with more
+    (several per CU) or fewer, and for longer K, the main kernel runs."""
+    rows = lambda M, K, L: g.nvfp4_gemv_plan(M, K, L)["rows_per_wg"] == 32
+    assert rows(7168, 64, 1) and rows(7168, 4096, 1) and rows(3072, 4096, 2) and rows(8192, 2048, 1)
+    assert rows(6017, 2048, 1) and not rows(6016, 2048, 1)        # 192 workgroups; 188
+    assert not rows(8193, 2048, 1)                                # 260 workgroups
+    assert not rows(7168, 2048, 4) and not rows(7168, 4096, 3)    # several workgroups per CU
+    assert not rows(7168, 4128, 1) and not rows(1000, 4096, 3)    # longer K; a small grid
 
 
 def test_row_kernel_boundaries():

@@ -125,6 +125,87 @@ def check_row_shape(M, K, L, layout, p, ws_bytes, strides=None):
     assert np.array_equal(written, expect), "some output row is written zero or several times"
 
 
+def check_rows_shape(M, K, L, layout, p, ws_bytes, strides=None):
+    """The multi-row kernel (many rows, K <= 4096): workgroup (batch l, block
+    rb, line h) owns rows rb*128 + 8h + q + 32w (wave w, q < 8); lane j takes
+    chunks j, j+64 (clamped) of each. Blocked scales: the waves copy line h of
+    every tile of block rb into LDS (copy i: tiles 8i .. 8i+7, clamped) and
+    each (row, chunk) reads its pair back from there; plain scales: each row's
+    pairs from global memory. Lane 63 writes each live row's output."""
+    nchunks, nkb = K // 32, K // 16
+    ncb = cdiv(nkb, 4)
+    P = cdiv(M, 128) * 4
+    assert p["workgroups"] == L * P and p["rows_per_wg"] == 32 and p["k_splits"] == 1 and ws_bytes == 0
+    nsc = cdiv(ncb, 8)
+    assert p["lds_bytes"] == nsc * DMA_BYTES and nchunks <= 128
+    cpl = 1 if nchunks <= 64 else 2
+    sd = strides or g.nvfp4_gemv_dense_strides(M, K, L, layout)
+    a_row, a_bat, b_bat, c_bat = sd["a_row"], sd["a_batch"], sd["b_batch"], sd["c_batch"]
+    sfa_row, sfa_bat, sfb_bat = sd["sfa_row"], sd["sfa_batch"], sd["sfb_batch"]
+    a_bytes = (L - 1) * a_bat + (M - 1) * a_row + K // 2
+    b_size = (L - 1) * b_bat + K // 2
+    sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512
+    sfb_batch = nkb if layout == 0 else ncb * 512
+    sfa_size = (L - 1) * sfa_bat + ((M - 1) * sfa_row + nkb if layout == 0 else sfa_batch)
+    sfb_size = (L - 1) * sfb_bat + sfb_batch
+    n_wg = p["workgroups"]
+    lids = xcd_remap(np.arange(n_wg), n_wg)
+    assert np.array_equal(np.sort(lids), np.arange(n_wg)), "remap is not a bijection"
+    lane = np.arange(64)
+    written = np.zeros((L - 1) * c_bat + M, np.int64)
+    taken = np.zeros((L, M, nchunks), np.int64)
+    for lid in lids:
+        l, t = lid // P, lid % P
+        rb, h = t >> 2, t & 3
+        assert l < L
+        lds = np.full(nsc * DMA_BYTES, -1, np.int64)   # global SFA byte each LDS byte holds
+        if layout == 1:
+            for w in range(4):
+                for i in range(w, nsc, 4):
+                    tile = np.minimum(8 * i + (lane >> 3), ncb - 1)
+                    src = l * sfa_bat + (rb * ncb + tile) * 512 + h * 128 + (lane & 7) * 16
+                    assert src.min() >= 0 and (src + 16).max() <= sfa_size, "SFA copy outside the tensor"
+                    dst = i * DMA_BYTES + lane * 16
+                    assert (dst + 16).max() <= lds.size, "SFA copy outside the LDS"
+                    for b in range(16):
+                        lds[dst + b] = src + b
+        for w in range(4):
+            for i in range(cpl):
+                c = lane + 64 * i
+                live = c < nchunks
+                cc = np.minimum(c, nchunks - 1)
+                b_off = l * b_bat + cc * 16
+                assert b_off.min() >= 0 and (b_off + 16).max() <= b_size, "B read outside the tensor"
+                sb = l * sfb_bat + sf_offset(layout, np.zeros_like(cc), 2 * cc, nkb, ncb)
+                assert sb.min() >= 0 and (sb + 2).max() <= sfb_size and (sb % 2 == 0).all()
+                for q in range(8):
+                    r_real = rb * 128 + 8 * h + q + 32 * w
+                    r = min(r_real, M - 1)
+                    a_off = l * a_bat + r * a_row + cc * 16
+                    assert a_off.min() >= 0 and (a_off + 16).max() <= a_bytes, "A read outside the tensor"
+                    if layout == 0:
+                        sa = l * sfa_bat + r * sfa_row + 2 * cc
+                        assert sa.min() >= 0 and (sa + 2).max() <= sfa_size
+                        got = [sa, sa + 1]
+                    else:
+                        off = (cc >> 1) * 128 + q * 16 + w * 4 + (cc & 1) * 2
+                        assert (off + 2).max() <= lds.size, "SFA read outside the LDS"
+                        got = [lds[off], lds[off + 1]]
+                    if r_real < M:
+                        for b in range(2):
+                            want = l * sfa_bat + (r * sfa_row + 2 * cc + b if layout == 0
+                                                  else sf_offset(1, np.full_like(cc, r), 2 * cc + b, nkb, ncb))
+                            assert np.array_equal(got[b], want), "SFA pair is not the chunk's two scales"
+                        np.add.at(taken, (l, r_real, cc[live]), 1)
+                        if i == 0:
+                            written[l * c_bat + r_real] += 1
+    assert (taken == 1).all(), "some (row, chunk) is taken zero or several times"
+    expect = np.zeros_like(written)
+    for l in range(L):
+        expect[l * c_bat + np.arange(M)] += 1
+    assert np.array_equal(written, expect), "some output row is written zero or several times"
+
+
 def check_wide_row_shape(M, K, L, layout, p, ws_bytes, strides=None):
     """The wide-row kernel (few rows, longer K): a workgroup of 4 waves owns
     one row (workgroup lid: row lid % M of batch lid // M); thread j loads
@@ -192,6 +273,8 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     THREADS, CPL, PREFETCH = threads, cpl, prefetch
     p = (plan or g.nvfp4_gemv_plan)(M, K, L)
     ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
+    if p["threads_per_wg"] == ROW_THREADS and p["rows_per_wg"] == 32:
+        return check_rows_shape(M, K, L, layout, p, ws_bytes, strides)
     if p["threads_per_wg"] == ROW_THREADS and p["rows_per_wg"] == 1:
         return check_wide_row_shape(M, K, L, layout, p, ws_bytes, strides)
     if p["threads_per_wg"] == ROW_THREADS:
@@ -390,7 +473,10 @@ SHAPES = sorted({(w.M, w.K, w.L) for w in synth.ALL} |
                  (1, 352, 1), (1, 384, 1), (1, 320, 1), (128, 256, 1), (300, 4128, 1),
                  (127, 65536, 3), (121, 65536, 2), (16, 32768, 1), (1, 1 << 22, 1),
                  # wide-row kernel: K between 4096 and 32768, at most 400 rows
-                 (127, 32768, 3), (33, 4160, 2), (100, 8256, 3), (400, 20480, 1), (33, 4128, 2)})
+                 (127, 32768, 3), (33, 4160, 2), (100, 8256, 3), (400, 20480, 1), (33, 4128, 2),
+                 # multi-row kernel: K <= 4096, grids of 192 .. 256 workgroups (ragged M and
+                 # K, a partial last copy of SFA lines, rows past M in the last block)
+                 (6017, 2048, 1), (3072, 4096, 2), (7168, 96, 1), (8100, 1056, 1), (2000, 3104, 3)})
 
 
 @pytest.mark.parametrize("M,K,L", SHAPES)
@@ -419,6 +505,10 @@ STRIDED = [  # (M, K, L, layout, stride overrides)
                            sfa_batch=32768 + 512, sfb_batch=32768 + 1024, c_batch=130)),
     (100, 2048, 2, 0, dict(a_row=1024 + 32, a_batch=100 * 1056 + 16, b_batch=1024 + 16, sfa_row=128 + 16,
                            sfa_batch=100 * 144 + 32, sfb_batch=160, c_batch=104)),
+    # the multi-row kernel with the caller's strides
+    (7000, 2048, 1, 1, dict(a_row=1024 + 48, c_batch=7000)),
+    (3000, 2048, 2, 0, dict(a_row=1024 + 16, a_batch=3000 * 1040 + 32, b_batch=1024 + 32, sfa_row=128 + 32,
+                            sfa_batch=3000 * 160 + 16, sfb_batch=144, c_batch=3008)),
 ]
 
 

@@ -1097,7 +1097,11 @@ Plan make_plan(int64_t M, int64_t K, int64_t L, int nv = 1)
             }
         }
     }
-    const int64_t kc = cdiv(nchunks, S);
+    // chunks per slice: a multiple of 8, so that every slice starts on a
+    // 4-block group (the blocked scales are staged, and their pairs indexed,
+    // by groups of two chunks counted from the slice's first chunk) and plain
+    // scale rows stay in 16-byte units
+    const int64_t kc = S == 1 ? nchunks : cdiv(cdiv(nchunks, S), 8) * 8;
     S = cdiv(nchunks, kc);
     pl.S = (int)S;
     pl.kc_split = (int)kc;

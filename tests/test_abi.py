@@ -156,6 +156,17 @@ def test_plans(w):
         assert p["threads_per_wg"] == 320      # 4 computing waves and the staging wave
 
 
+def test_split_slices_start_on_scale_groups():
+    """With a K-split, every slice is a multiple of 8 chunks (256 k), so each
+    starts on a 4-block scale group, and the slices cover K."""
+    for M, K, L in [(102, 55872, 2), (90, 46272, 1), (64, 65536, 1), (5, 32768, 2), (1, 1 << 22, 1),
+                    (30, 60768, 2), (127, 65536, 3)]:
+        p = g.nvfp4_gemv_plan(M, K, L)
+        if p["k_splits"] > 1:
+            assert p["k_per_split"] % 256 == 0, (M, K, L, p)
+            assert p["k_splits"] * p["k_per_split"] >= K > (p["k_splits"] - 1) * p["k_per_split"]
+
+
 def test_multi_row_kernel_boundaries():
     """The multi-row kernel takes short rows (K <= 4096, not the row kernel's)
     where its grid of 32-row workgroups is 192 to 256 workgroups; with more

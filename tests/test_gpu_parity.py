@@ -166,7 +166,10 @@ ODD = [(1, 32, 1), (2, 64, 3), (31, 96, 2), (33, 160, 1), (129, 2080, 2), (300, 
        (1, 16384, 1), (5, 32768, 1), (257, 7168, 2), (64, 224, 5), (1000, 1024, 1), (3, 4096, 7),
        (64, 65536, 1), (300, 20480, 2),
        # the multi-row kernel: ragged M and K, a partial last copy of SFA lines
-       (6017, 2048, 1), (7168, 96, 1), (8100, 1056, 1), (2000, 3104, 3)]
+       (6017, 2048, 1), (7168, 96, 1), (8100, 1056, 1), (2000, 3104, 3),
+       # K-splits whose chunk count does not divide evenly: the slices start on
+       # 4-block groups (an odd chunk count per slice once read the wrong pairs)
+       (102, 55872, 2), (90, 46272, 1)]
 
 
 @pytest.mark.parametrize("M,K,L", ODD)

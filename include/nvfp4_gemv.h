@@ -249,13 +249,17 @@ nvfp4_status_t nvfp4_gemm_small_n(const void *a, const void *b, const void *sfa,
                                   float alpha, void *stream);
 
 /* Launch plan of nvfp4_gemm_small_n's own kernels for a shape and scale
- * layout: rows per workgroup, workgroups (256 threads each) and dynamic LDS
- * bytes. From N = 3 the workgroups own 32 rows; with blocked scales, where B,
- * the SFB lines and a workgroup's SFA lines fit in LDS (about (3N/4 + 2) * K
- * bytes within 150 KiB: K up to 16384 for N = 8, 32768 for N = 3), they are
- * staged there (lds_bytes > 0) and each 128-row block has 4 workgroups. Any
- * output pointer may be NULL. Returns NVFP4_ERR_INVALID_SHAPE for shapes it
- * does not take, NVFP4_ERR_INVALID_LAYOUT for an unknown layout. */
+ * layout: rows per workgroup, workgroups and dynamic LDS bytes (for N = 1 or
+ * 2 where the GEMV's kernel runs instead, the plan of the dot-product kernel
+ * that would run otherwise). The matrix-core kernels (N >= 3, and N = 2 on
+ * large blocked shapes) give each workgroup 32 rows, 4 workgroups per 128-row
+ * block. With blocked scales they stage B, the SFB dwords and the workgroup's
+ * SFA lines in LDS: grids of more than 256 workgroups stage all of K at once
+ * where that fits in 150 KiB (about (3N/4 + 2) * K bytes; 256 threads per
+ * workgroup), other grids stream K through three slots of 32 K-steps (52 KiB
+ * for N <= 4, 78 KiB up to N = 8; 320 threads per workgroup). Plain scales:
+ * no LDS. Any output pointer may be NULL. Returns NVFP4_ERR_INVALID_SHAPE for
+ * shapes it does not take, NVFP4_ERR_INVALID_LAYOUT for an unknown layout. */
 nvfp4_status_t nvfp4_gemm_small_n_plan(int64_t M, int64_t N, int64_t K, int64_t L, int sf_layout,
                                        int32_t *rows_per_wg, int64_t *workgroups, int32_t *lds_bytes);
 

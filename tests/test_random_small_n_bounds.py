@@ -34,7 +34,7 @@ def route(M, N, K, L, layout):
     return "dot"
 
 
-def random_small_n_shapes(seed=77, n=25):
+def random_small_n_shapes(seed=77, n=40):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):

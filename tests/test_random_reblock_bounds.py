@@ -9,14 +9,14 @@ import synth
 from test_reblock_bounds import emulate, tiles_of
 
 
-def random_reblock_shapes(seed=909, n=12):
+def random_reblock_shapes(seed=909, n=10):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        if i % 3 == 0:    # many batches or long rows: grids that take 32 tiles
-            rows, K, L = int(rng.integers(100, 1100)), 64 * int(rng.integers(200, 260)), int(rng.integers(2, 9))
+        if i % 3 == 0:    # grids that take 32 tiles (256 workgroups or more of 128 rows x 128 columns)
+            rows, K, L = int(rng.integers(1, 129)), 2048 * int(rng.integers(8, 11)), int(rng.integers(32, 41))
         else:
-            rows, K, L = int(rng.integers(1, 3000)), 32 * int(rng.integers(1, 400)), int(rng.integers(1, 5))
+            rows, K, L = int(rng.integers(1, 1000)), 32 * int(rng.integers(1, 300)), int(rng.integers(1, 4))
         out.append((rows, K, L))
     return out
 

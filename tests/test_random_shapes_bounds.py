@@ -8,7 +8,7 @@ import pytest
 from test_kernel_bounds import check_shape
 
 
-def random_shapes(seed=2026, n=50):
+def random_shapes(seed=2026, n=30):
     """Shapes drawn per branch: short rows and few rows, longer K and few
     rows, short K on about one workgroup per CU, general shapes (ragged M, K a
     multiple of 32, up to 8 batches) and few rows with long K (K-splits), each

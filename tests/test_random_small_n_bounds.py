@@ -34,7 +34,7 @@ def route(M, N, K, L, layout):
     return "dot"
 
 
-def random_small_n_shapes(seed=77, n=40):
+def random_small_n_shapes(seed=77, n=25):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -51,8 +51,8 @@ def random_small_n_shapes(seed=77, n=40):
             M, N, K, L = (int(rng.integers(1, 2000)), int(rng.integers(3, 9)), 32 * int(rng.integers(1, 400)),
                           int(rng.integers(1, 4)))
         else:              # N = 3..8, many batches: the up-front kernel (blocked)
-            M, N, K, L = (int(rng.integers(1, 300)), int(rng.integers(3, 9)), 32 * int(rng.integers(1, 200)),
-                          int(rng.integers(40, 90)))
+            M, N, K, L = (int(rng.integers(129, 257)), int(rng.integers(3, 9)), 32 * int(rng.integers(1, 160)),
+                          int(rng.integers(33, 45)))
         out.append((M, N, K, L))
     return out
 

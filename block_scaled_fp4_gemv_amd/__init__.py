@@ -46,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "nvfp4_gemv_strided",
     "nvfp4_gemv_dense_strides",
     "nvfp4_gemv_plan",
+    "nvfp4_gemv_two_vectors_plan",
     "nvfp4_gemm_small_n",
     "nvfp4_gemm_small_n_plan",
     "nvfp4_scales_to_blocked",
@@ -122,6 +123,8 @@ def lib():
     L.nvfp4_gemv_workspace_bytes.argtypes = [i64, i64, i64]
     L.nvfp4_gemv_plan.restype = i32
     L.nvfp4_gemv_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    L.nvfp4_gemv_two_vectors_plan.restype = i32
+    L.nvfp4_gemv_two_vectors_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
     L.nvfp4_gemm_small_n.restype = i32
     L.nvfp4_gemm_small_n.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.c_float, vp]
     L.nvfp4_gemm_small_n_plan.restype = i32
@@ -297,6 +300,14 @@ def nvfp4_gemv_plan(M: int, K: int, L: int) -> dict:
     st = lib().nvfp4_gemv_plan(M, K, L, ctypes.byref(plan))
     if st != NVFP4_OK:
         raise Nvfp4Error(st, "nvfp4_gemv_plan")
+    return plan.as_dict()
+
+
+def nvfp4_gemv_two_vectors_plan(M: int, K: int, L: int) -> dict:
+    plan = Plan()
+    st = lib().nvfp4_gemv_two_vectors_plan(M, K, L, ctypes.byref(plan))
+    if st != NVFP4_OK:
+        raise Nvfp4Error(st, "nvfp4_gemv_two_vectors_plan")
     return plan.as_dict()
 
 

@@ -1679,6 +1679,26 @@ nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *pl
     return NVFP4_OK;
 }
 
+nvfp4_status_t nvfp4_gemv_two_vectors_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan)
+{
+    if (!plan)
+        return NVFP4_ERR_NULL_POINTER;
+    nvfp4_status_t st = check_shape(M, K, L);
+    if (st != NVFP4_OK)
+        return st;
+    const Plan pl = make_plan(M, K, L, 2);
+    if (pl.S > 1 || L * 2 * M > INT32_MAX / 2)
+        return NVFP4_ERR_INVALID_SHAPE;
+    plan->lanes_per_row = pl.lpr;
+    plan->rows_per_wg = 4 * pl.spw;
+    plan->k_splits = pl.S;
+    plan->k_per_split = pl.kc_split * 32;
+    plan->workgroups = pl.n_wg;
+    plan->threads_per_wg = kBlock;
+    plan->lds_bytes = pl.lds_bytes;
+    return NVFP4_OK;
+}
+
 const char *nvfp4_status_string(int status)
 {
     switch (status) {

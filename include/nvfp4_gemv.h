@@ -221,6 +221,14 @@ typedef struct {
 nvfp4_status_t nvfp4_gemv_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan);
 
 /*
+ * Launch plan of the GEMV kernel with two right-hand vectors, which
+ * nvfp4_gemm_small_n runs for N = 2 where no matrix-core kernel applies and
+ * the GEMV's plan needs no K-split (for tests and reports; fields as for
+ * nvfp4_gemv_plan). NVFP4_ERR_INVALID_SHAPE where that kernel does not run.
+ */
+nvfp4_status_t nvfp4_gemv_two_vectors_plan(int64_t M, int64_t K, int64_t L, nvfp4_plan_t *plan);
+
+/*
  * Block-scaled skinny GEMM with N = 1..8 right-hand vectors (the general
  * product kernelbot NVFP4 GEMV submission 103289 hands to torch._scaled_mm,
  * a @ b^T with block scales and a float16 result; the GEMV is N = 1):

@@ -13,7 +13,7 @@ if not torch.cuda.is_available():
 
 from test_gpu_small_n import run_small_n  # noqa: E402
 from test_oracle_small_n import inputs  # noqa: E402
-from test_random_small_n_bounds import SHAPES, route  # noqa: E402
+from test_random_small_n_bounds import SHAPES  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -25,9 +25,7 @@ def _oracle_built():
 def test_random_small_n_parity(M, N, K, L):
     a, b, sfa, sfb = inputs(M, N, K, L, 3 * M + N + K + L)
     ref = oracle.gemm_small_n(a, b, sfa, sfb, M, N, K, L)
-    for layout_id, layout in ((0, "plain"), (1, "blocked")):
-        if route(M, N, K, L, layout_id) == "gemv2":
-            continue                    # no CPU mirror of that path; fixed GPU cases cover it
+    for layout in ("plain", "blocked"):
         got = run_small_n(a, b, sfa, sfb, M, N, K, L, layout)
         rep = oracle.check_report(got, ref)
         assert rep == "", f"{M}x{N}x{K}x{L} [{layout}]\n{rep}"

@@ -265,14 +265,33 @@ def check_wide_row_shape(M, K, L, layout, p, ws_bytes, strides=None):
     assert np.array_equal(written, expect), "some output row is written zero or several times"
 
 
+def two_vector_strides(M, K, L, layout):
+    """The operands of the GEMV kernel with two vectors (nvfp4_gemm_small_n,
+    N = 2): B [L][2][K/2], SFB per vector a row (plain) or the next 16-byte line
+    of each tile (blocked), C [L][2][M]; plus the offsets between the vectors."""
+    sd = g.nvfp4_gemv_dense_strides(M, K, L, layout)
+    nkb = K // 16
+    sd.update(b_batch=K, c_batch=2 * M, b_vec=K // 2, c_vec=M,
+              sfb_vec=nkb if layout == 0 else 16)
+    if layout == 0:
+        sd["sfb_batch"] = 2 * nkb
+    return sd
+
+
 def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREADS, cpl=CPL,
-                prefetch=PREFETCH, max_tickets=MAX_TICKETS, strides=None):
+                prefetch=PREFETCH, max_tickets=MAX_TICKETS, strides=None, nv=1):
     """Walk the whole grid of one launch. ``plan``/``workspace_bytes`` default
     to the built library's; the constants can be overridden to check a variant.
-    ``strides`` (nvfp4_strides_t fields) default to the dense layout."""
+    ``strides`` (nvfp4_strides_t fields) default to the dense layout. ``nv`` = 2:
+    the main kernel with two right-hand vectors, as the N-vector GEMM runs it."""
     THREADS, CPL, PREFETCH = threads, cpl, prefetch
-    p = (plan or g.nvfp4_gemv_plan)(M, K, L)
-    ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
+    if nv == 2:
+        p = (plan or g.nvfp4_gemv_two_vectors_plan)(M, K, L)
+        ws_bytes = 0
+        strides = strides or two_vector_strides(M, K, L, layout)
+    else:
+        p = (plan or g.nvfp4_gemv_plan)(M, K, L)
+        ws_bytes = (workspace_bytes or g.nvfp4_gemv_workspace_bytes)(M, K, L)
     if p["threads_per_wg"] == ROW_THREADS and p["rows_per_wg"] == 32:
         return check_rows_shape(M, K, L, layout, p, ws_bytes, strides)
     if p["threads_per_wg"] == ROW_THREADS and p["rows_per_wg"] == 1:
@@ -291,20 +310,22 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     stb = stage_bytes(lpr, spw)
     bstb = cdiv(64 * lpr, DMA_BYTES) * DMA_BYTES if STAGE_B else 0
     sfbb = cdiv(32 * lpr, DMA_BYTES) * DMA_BYTES
-    assert lds_bytes == stb + bstb + sfbb + 4 * spw * WPG * 4
+    assert lds_bytes == stb + nv * (bstb + sfbb) + 4 * spw * nv * WPG * 4
     assert lds_bytes <= 159 * 1024            # a workgroup fits the CU's 160 KiB of LDS
     sd = strides or g.nvfp4_gemv_dense_strides(M, K, L, layout)
     a_row, a_bat, b_bat, c_bat = sd["a_row"], sd["a_batch"], sd["b_batch"], sd["c_batch"]
     sfa_row, sfa_bat, sfb_bat = sd["sfa_row"], sd["sfa_batch"], sd["sfb_batch"]
+    b_vec, sfb_vec, c_vec = sd.get("b_vec", 0), sd.get("sfb_vec", 0), sd.get("c_vec", 0)
+    assert nv == 1 or S == 1, "several vectors only without a K-split"
     wide_plain = nchunks % 8 == 0 and kc % 8 == 0 and sfa_row % 16 == 0 and sfa_bat % 16 == 0
     direct = layout == 0 and not wide_plain
     # extents: one past the last byte each operand's strides address
     a_bytes = (L - 1) * a_bat + (M - 1) * a_row + K // 2
-    b_size = (L - 1) * b_bat + K // 2
+    b_size = (L - 1) * b_bat + (nv - 1) * b_vec + K // 2
     sfa_batch = M * nkb if layout == 0 else cdiv(M, 128) * ncb * 512     # dense bytes of one batch
     sfb_batch = nkb if layout == 0 else ncb * 512
     sfa_size = (L - 1) * sfa_bat + ((M - 1) * sfa_row + nkb if layout == 0 else sfa_batch)
-    sfb_size = (L - 1) * sfb_bat + sfb_batch
+    sfb_size = (L - 1) * sfb_bat + (nv - 1) * (sfb_vec if layout == 0 else 0) + sfb_batch
 
     def sfa_addr(l, r, kb):                     # global byte of scale (r, kb) of batch l
         if layout == 0:
@@ -313,10 +334,11 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
     valid_sfa = np.zeros(sfa_batch, bool)       # bytes that hold a real scale (dense batch)
     rr, kk = np.meshgrid(np.arange(M), np.arange(nkb), indexing="ij")
     valid_sfa[sf_offset(layout, rr, kk, nkb, ncb)] = True
-    valid_sfb = np.zeros(sfb_batch, bool)
-    valid_sfb[sf_offset(layout, np.zeros(nkb, np.int64), np.arange(nkb), nkb, ncb)] = True
+    valid_sfb = np.zeros(sfb_batch + (nv - 1) * sfb_vec, bool)   # vector v's scale (kb) at v * sfb_vec + ...
+    for v in range(nv):
+        valid_sfb[v * sfb_vec + sf_offset(layout, np.zeros(nkb, np.int64), np.arange(nkb), nkb, ncb)] = True
 
-    written = np.zeros((L - 1) * c_bat + M, np.int64)
+    written = np.zeros((L - 1) * c_bat + (nv - 1) * c_vec + M, np.int64)
     lids = xcd_remap(np.arange(n_wg), n_wg)
     assert np.array_equal(np.sort(lids), np.arange(n_wg)), "remap is not a bijection"
     tid = np.arange(THREADS)
@@ -390,41 +412,45 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
             # ---- b' inputs staged by the staging wave (blocked layout): B
             # chunks, then the 16-byte line of each 4-block SFB group that holds row 0
             stage_b = layout == 1 and STAGE_B
-            b_src = np.full(bstb, -1, np.int64)
-            for i in range(cdiv(nck, 64) if stage_b else 0):
-                src = l * b_bat + (c0 + np.minimum(i * 64 + lane, nck - 1)) * 16
-                assert src.min() >= 0 and (src + 16).max() <= b_size and (src % 16 == 0).all()
-                dst = i * DMA_BYTES + lane * 16
-                assert (dst + 16).max() <= bstb, "staged B outside its area"
-                for b in range(16):
-                    b_src[dst + b] = src + b
-            sfb_src = np.full(sfbb, -1, np.int64)
+            b_src = np.full(nv * bstb, -1, np.int64)                # vector v's B at v * bstb
+            for v in range(nv):
+                for i in range(cdiv(nck, 64) if stage_b else 0):
+                    src = l * b_bat + v * b_vec + (c0 + np.minimum(i * 64 + lane, nck - 1)) * 16
+                    assert src.min() >= 0 and (src + 16).max() <= b_size and (src % 16 == 0).all()
+                    dst = v * bstb + i * DMA_BYTES + lane * 16
+                    assert (dst + 16).max() <= (v + 1) * bstb, "staged B outside its area"
+                    for b in range(16):
+                        b_src[dst + b] = src + b
+            sfb_src = np.full(nv * sfbb, -1, np.int64)              # vector v's SFB lines at v * sfbb
             if layout == 1:
-                for i in range(cdiv(ncb_seg, 64)):
-                    src = l * sfb_bat + (cb0 + np.minimum(i * 64 + lane, ncb_seg - 1)) * 512
-                    assert src.min() >= 0 and (src + 16).max() <= sfb_size and (src % 16 == 0).all()
-                    dst = i * DMA_BYTES + lane * 16
-                    assert (dst + 16).max() <= sfbb, "staged SFB outside its area"
-                    for b in range(16):
-                        sfb_src[dst + b] = src + b
-            # ---- b': each lane's B chunk and its two SFB scales
-            for k in range(CPL):
-                cc = np.minimum(j + k * lpr, nck - 1)
-                ci = c0 + cc
-                if stage_b:
-                    for b in range(16):
-                        assert np.array_equal(b_src[cc * 16 + b], l * b_bat + ci * 16 + b), "staged B mismatch"
-                else:
-                    boff = l * b_bat + ci * 16
-                    assert boff.min() >= 0 and (boff + 16).max() <= b_size and (boff % 16 == 0).all()
-                so = sf_offset(layout, np.zeros_like(ci), 2 * ci, nkb, ncb)
-                assert (so + 1).max() < sfb_batch and (l * sfb_bat + so + 2).max() <= sfb_size
-                assert valid_sfb[so].all() and valid_sfb[so + 1].all()
-                if layout == 1:
-                    at = (cc >> 1) * 16 + (cc & 1) * 2
-                    assert (at + 2).max() <= sfbb
-                    assert np.array_equal(sfb_src[at], l * sfb_bat + so), "staged SFB mismatch"
-                    assert np.array_equal(sfb_src[at + 1], l * sfb_bat + so + 1), "staged SFB mismatch"
+                for v in range(nv):
+                    for i in range(cdiv(ncb_seg, 64)):
+                        src = l * sfb_bat + v * sfb_vec + (cb0 + np.minimum(i * 64 + lane, ncb_seg - 1)) * 512
+                        assert src.min() >= 0 and (src + 16).max() <= sfb_size and (src % 16 == 0).all()
+                        dst = v * sfbb + i * DMA_BYTES + lane * 16
+                        assert (dst + 16).max() <= (v + 1) * sfbb, "staged SFB outside its area"
+                        for b in range(16):
+                            sfb_src[dst + b] = src + b
+            # ---- b': each lane's B chunk and its two SFB scales, per vector
+            for v in range(nv):
+                for k in range(CPL):
+                    cc = np.minimum(j + k * lpr, nck - 1)
+                    ci = c0 + cc
+                    if stage_b:
+                        for b in range(16):
+                            assert np.array_equal(b_src[v * bstb + cc * 16 + b], l * b_bat + v * b_vec + ci * 16 + b), \
+                                "staged B mismatch"
+                    else:
+                        boff = l * b_bat + v * b_vec + ci * 16
+                        assert boff.min() >= 0 and (boff + 16).max() <= b_size and (boff % 16 == 0).all()
+                    so = v * sfb_vec + sf_offset(layout, np.zeros_like(ci), 2 * ci, nkb, ncb)
+                    assert (so + 1).max() < valid_sfb.size and (l * sfb_bat + so + 2).max() <= sfb_size
+                    assert valid_sfb[so].all() and valid_sfb[so + 1].all()
+                    if layout == 1:
+                        at = v * sfbb + (cc >> 1) * 16 + (cc & 1) * 2
+                        assert (at + 2).max() <= (v + 1) * sfbb
+                        assert np.array_equal(sfb_src[at], l * sfb_bat + so), "staged SFB mismatch"
+                        assert np.array_equal(sfb_src[at + 1], l * sfb_bat + so + 1), "staged SFB mismatch"
 
             # ---- computing waves: lane j reads, for its chunk k and round row q,
             # the 2 bytes at sfoff(c) + rowpart(q) (c, q clamped as in the kernel)
@@ -450,7 +476,8 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
         # ---- outputs
         real = rows_all[rows_all < M]
         if S == 1 or s == S - 1:
-            np.add.at(written, l * c_bat + real, 1)
+            for v in range(nv):
+                np.add.at(written, l * c_bat + v * c_vec + real, 1)
         if S > 1:
             assert P * L <= max_tickets, "more tickets than the ticket region holds"
             ws_part = cdiv(L * M * S * 4, 256) * 256
@@ -459,7 +486,8 @@ def check_shape(M, K, L, layout, plan=None, workspace_bytes=None, threads=THREAD
             assert l * P + tile < P * L
     expect = np.zeros_like(written)
     for l in range(L):
-        expect[l * c_bat + np.arange(M)] += 1
+        for v in range(nv):
+            expect[l * c_bat + v * c_vec + np.arange(M)] += 1
     assert np.array_equal(written, expect), "some output row is written zero or several times"
 
 
@@ -483,6 +511,17 @@ SHAPES = sorted({(w.M, w.K, w.L) for w in synth.ALL} |
 @pytest.mark.parametrize("layout", [0, 1])
 def test_kernel_addresses_in_bounds(M, K, L, layout):
     check_shape(M, K, L, layout)
+
+
+# the main kernel with two vectors (the N-vector GEMM's N = 2 without a K-split)
+TWO_VECTORS = [(1, 32, 1), (33, 160, 5), (1000, 4096, 3), (300, 20480, 2), (127, 16384, 1), (4100, 256, 1),
+               (1012, 4352, 3), (7168, 2048, 1), (129, 2080, 2), (7168, 16384, 1)]
+
+
+@pytest.mark.parametrize("M,K,L", TWO_VECTORS)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_two_vector_kernel_addresses_in_bounds(M, K, L, layout):
+    check_shape(M, K, L, layout, nv=2)
 
 
 def strided(M, K, L, layout, **over):

@@ -3,10 +3,9 @@ that every routing branch is hit: N = 1 (the GEMV's kernels), N = 2 (the
 dot-product kernel, or the matrix-core kernels on large blocked shapes) and
 N = 3..8 (streamed or up-front staged kernels for blocked scales, the unstaged
 kernel for plain scales). For each shape and layout the CPU mirror of the
-kernel the library picks walks its whole grid. Shapes that take the GEMV
-kernel with two vectors (N = 2, no matrix-core kernel) are left out here and
-covered by the fixed GPU cases. The same shapes run on the GPU against the
-oracle in test_gpu_random_small_n.py."""
+kernel the library picks walks its whole grid (the GEMV kernel with two
+vectors included). The same shapes run on the GPU against the oracle in
+test_gpu_random_small_n.py."""
 import numpy as np
 import pytest
 
@@ -65,7 +64,7 @@ def mirror(M, N, K, L, layout):
     if kind == "gemv":
         check_shape(M, K, L, layout)
     elif kind == "gemv2":
-        pytest.skip("the GEMV kernel with two vectors: fixed GPU cases only")
+        check_shape(M, K, L, layout, nv=2)
     elif kind == "dot":
         dot_mirror.check(M, N, K, L, layout)
     elif kind == "unstaged":
@@ -86,4 +85,4 @@ def test_random_small_n_addresses(M, N, K, L, layout):
 
 def test_random_small_n_shapes_cover_the_kernels():
     kinds = {route(M, N, K, L, lay) for M, N, K, L in SHAPES for lay in (0, 1)}
-    assert {"gemv", "dot", "unstaged", "streamed", "upfront"} <= kinds, kinds
+    assert {"gemv", "gemv2", "dot", "unstaged", "streamed", "upfront"} <= kinds, kinds

@@ -58,7 +58,9 @@ CASES = [(1, 1, 32, 1), (7, 3, 96, 2), (128, 2, 2048, 1), (300, 4, 20480, 2), (1
          (1000, 4, 7168, 2), (128, 4, 1280, 5), (20, 3, 64, 1), (7168, 3, 16384, 1),
          # N = 2 on the matrix-core kernels (blocked, K >= 4096, 128 workgroups or
          # more): streamed, up-front; and short rows through the GEMV kernel
-         (4100, 2, 4224, 1), (2000, 2, 4224, 5), (4100, 2, 256, 1)]
+         (4100, 2, 4224, 1), (2000, 2, 4224, 5), (4100, 2, 256, 1),
+         # wide grids with a ragged last 128-row block, two batches
+         (5000, 5, 1056, 1), (3000, 8, 4160, 2)]
 
 
 @pytest.mark.parametrize("M,N,K,L", CASES)

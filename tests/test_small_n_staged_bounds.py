@@ -178,7 +178,10 @@ def emulate(M, N, K, L):
                                      (256, 8, 16384, 1), (200, 3, 2048, 4), (100, 6, 7168, 2),
                                      (40, 4, 4224, 1), (20, 8, 40960, 1), (64, 3, 512, 1),
                                      # N = 2 (blocked, K >= 4096, 128 workgroups or more)
-                                     (4100, 2, 4224, 1), (2000, 2, 4224, 2)])
+                                     (4100, 2, 4224, 1), (2000, 2, 4224, 2),
+                                     # wide grids, ragged last 128-row blocks, two batches
+                                     (7168, 3, 256, 1), (5000, 5, 128, 1), (6000, 3, 224, 1),
+                                     (3000, 8, 128, 2), (1000, 4, 4096, 3)])
 def test_staged_kernel_indexing(M, N, K, L):
     taken, written = emulate(M, N, K, L)
     assert np.all(taken == 1), "each (row, chunk) of A is taken exactly once"
